@@ -1,0 +1,215 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) implementation of the
+ * DeepSeek Sparse Attention (DSA) hot path:
+ *
+ *   dsa_index_score   lightning-indexer score of every cached key slot
+ *   dsa_topk          the index_topk best attendable slots (unordered set)
+ *   dsa_sparse_attn   top-k sparse multi-query attention with attention sink
+ *   dsa_decode_step   the three fused into one decode step on one stream,
+ *                     with the always-selected sliding window
+ *
+ * Sources (web pages, cited by title and section):
+ *   [NKI-V32]   AWS Neuron "DeepSeek-V3.2 Sparse Indexer Kernel API Reference"
+ *   [NKI-MX]    AWS Neuron "Sparse Attention Indexer MX BF16Score Kernel API Reference"
+ *   [NEMO-DSV4] NeMo AutoModel API page
+ *               "nemo_automodel.components.models.deepseek_v4.optimized_kernels"
+ *   [V4-KERNEL] kwkr.cn article on DeepSeek-V4-Pro-0813-nvfp4-DSpark
+ *               inference/kernel.py (sparse-attention and FP8 sections)
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE memory on the current HIP device, owned by
+ *     the caller, dense row-major in the layout stated, 16-byte aligned.
+ *     The library never allocates, frees or keeps a pointer; scratch space
+ *     is the caller's `workspace` (size from the matching *_workspace_size
+ *     query, which needs no GPU).
+ *   - All work is enqueued on `stream` (NULL = the default stream); no call
+ *     synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error status no output has been touched.  DSA_ERR_LAUNCH reports a
+ *     launch failure; faults during execution surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this interface.  Calls are
+ *     thread-safe; the library holds no state.
+ *   - bf16 = bfloat16; fp8 = OCP FP8 E4M3 ("e4m3fn", max 448) bytes.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,        /* a required pointer is NULL */
+    DSA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    DSA_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+    DSA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    DSA_ERR_LAUNCH = 6       /* a kernel launch failed (hipGetLastError) */
+} dsa_status_t;
+
+typedef enum dsa_key_dtype {
+    DSA_KEY_BF16 = 0,     /* key cache in bfloat16 */
+    DSA_KEY_FP8_E4M3 = 1  /* OCP FP8 E4M3 codes + one fp32 scale per slot */
+} dsa_key_dtype_t;
+
+/* flags of dsa_index_score */
+#define DSA_SCORE_RELU 1u /* per-head activation max(0, .) before weighting */
+
+#define DSA_INDEX_HEAD_DIM 128 /* indexer head_dim: [NKI-V32] Dimensions; [NKI-MX] usage */
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_ATTN_DIM 576
+
+/* Library version string, e.g. "0.1.0". */
+const char* dsa_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* dsa_status_string(dsa_status_t status);
+
+/* The finite mask bound written for slots a row cannot attend to:
+ * -0x1.FEp+127f, the most negative finite bfloat16, exact in fp32.  A finite
+ * bound (not -inf) keeps a bfloat16 consumer's max-select NaN-free
+ * [NKI-V32] Notes. */
+float dsa_mask_bound(void);
+
+/*
+ * dsa_index_score -- lightning-indexer scores [NKI-V32] Returns and Notes;
+ * [NKI-MX] :return: and Dimensions; [NEMO-DSV4] indexer_scores_torch.
+ *
+ *   scores[r, s] = scale * sum_h w[r, h] * phi( sum_d q[r, h, d] * K[c, s, d] )
+ *
+ * for every slot s < n_valid(r), where c = r / rows_per_seq is the cache row
+ * r reads and phi is the identity (flags = 0) or max(0, .) (DSA_SCORE_RELU).
+ * Slots s >= n_valid(r) get dsa_mask_bound() exactly.
+ *
+ * n_valid(r) = positions[r] + 1 if positions != NULL, else S_max; capped by
+ * valid_len when valid_len >= 0; clamped to [0, S_max] ([NKI-V32]
+ * Parameters positions / valid_len).  Decode: one row per sequence
+ * (rows_per_seq = 1).  Prefill: rows_per_seq query rows share one cache and
+ * positions[r] = start_pos + (r mod rows_per_seq) gives the causal range
+ * ([NKI-MX] Dimensions: end_pos = start_pos + S).
+ *
+ *   q        [M, H, D] bf16, device
+ *   w        [M, H] fp32 per-head weights, device
+ *   k_cache  [M / rows_per_seq, S_max, D] bf16, or fp8 E4M3 bytes, device
+ *   k_scale  [M / rows_per_seq, S_max] fp32, one scale per slot (fp8 only;
+ *            must be NULL for bf16)
+ *   positions [M] int32 or NULL, device
+ *   scores   [M, S_max] fp32 output, device
+ *
+ * Limits: D == 128; 1 <= H <= 128; M >= 1; S_max >= 1; M % rows_per_seq == 0.
+ * rows_per_seq == 1 requires flags == 0 (DSA_ERR_UNSUPPORTED otherwise).
+ * rows_per_seq > 1 requires bf16 keys and H <= 64.
+ */
+dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                             dsa_key_dtype_t k_dtype, const int32_t* positions, int32_t valid_len,
+                             int32_t M, int32_t rows_per_seq, int32_t H, int32_t D, int32_t S_max,
+                             float scale, uint32_t flags, float* scores, hipStream_t stream);
+
+/*
+ * dsa_topk -- per row, the min(index_topk, n_valid(r)) highest-scoring
+ * attendable slots, padded with -1 to width index_topk.  The row is an
+ * unordered set: column order carries no meaning ([NKI-V32] Returns and
+ * Notes; [NKI-MX] :param emit_flat_topk:).  Among equal scores at the
+ * selection boundary any subset of the right size may be returned.
+ *
+ *   scores      [M, S_max] fp32, device (NaN-free)
+ *   positions / valid_len: as dsa_index_score (rows_per_seq = 1 rule)
+ *   topk_idx    [M, index_topk] int32 output, device
+ *   topk_scores [M, index_topk] fp32 output or NULL: the selected scores,
+ *               -inf where the index is -1 ([NEMO-DSV4]
+ *               extract_indexer_topk_scores_torch)
+ *
+ * Limits: 1 <= index_topk <= DSA_MAX_TOPK; M >= 1; S_max >= 1.
+ */
+size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk);
+dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
+                      int32_t valid_len, int32_t index_topk, int32_t* topk_idx, float* topk_scores,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_attn -- top-k sparse multi-query attention with a learnable
+ * sink ([NEMO-DSV4] sparse_attention_torch; [V4-KERNEL] sparse-attention
+ * section).  For each batch b, query s and head h, over the listed entries
+ * j with 0 <= topk_idx[b, s, j] < S_kv (others, including -1, are masked and
+ * never read; listed entries count as a multiset):
+ *
+ *   logit_j = sm_scale * q[b, s, h, :] . kv[b, idx_j, :]
+ *   out     = sum_j e^{logit_j - m} kv[b, idx_j, 0:Dv]
+ *             / (sum_j e^{logit_j - m} + e^{attn_sink[h] - m}),  m = max_j logit_j
+ *   lse     = m + log(denominator)
+ *
+ * The sink is a logit in the units of the scaled scores; attn_sink = NULL
+ * removes the term.  With no valid entry, out = 0 and lse = attn_sink[h]
+ * (or -inf).
+ *
+ *   q         [B, S, Hq, Dqk] bf16, device
+ *   kv        [B, S_kv, Dqk] bf16, device (single head shared by all query
+ *             heads; the value is its leading Dv features)
+ *   attn_sink [Hq] fp32 or NULL, device
+ *   topk_idx  [B, S, K_top] int32, device
+ *   out       [B, S, Hq, Dv] bf16 output, device
+ *   lse       [B, S, Hq] fp32 output or NULL, device
+ *
+ * Limits: Dqk % 32 == 0, 32 <= Dqk <= 576; Dv % 16 == 0, 16 <= Dv <= Dqk;
+ * B, S, Hq, K_top >= 1; S_kv >= 1.
+ */
+size_t dsa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
+dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idx,
+                             int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
+                             int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_decode_step -- one DSA decode step for B sequences (one query token
+ * each): indexer score of every cached slot -> top-k -> index list =
+ * top-k plus the always-selected window of the last `window` attendable
+ * positions (a set union: top-k entries inside the window become -1;
+ * window positions below 0 are -1) -> sparse attention over that list
+ * ([V4-KERNEL] sparse-attention section, use in Attention.forward;
+ * [NEMO-DSV4] build_dsv4_sparse_topk_indices).  The key cache slot s and
+ * the kv slot s are the same position, so S_kv == S_max.
+ *
+ * The struct is versioned by struct_size (set it to sizeof(dsa_decode_args_t)).
+ */
+typedef struct dsa_decode_args {
+    size_t struct_size;
+    /* indexer */
+    const void* index_q;        /* [B, H, 128] bf16 */
+    const float* index_w;       /* [B, H] fp32 */
+    const void* k_cache;        /* [B, S_max, 128] bf16 or fp8 */
+    const float* k_scale;       /* [B, S_max] fp32 (fp8 only) or NULL */
+    dsa_key_dtype_t k_dtype;
+    const int32_t* positions;   /* [B] int32 or NULL */
+    int32_t valid_len;          /* < 0: none */
+    int32_t B, H, S_max;
+    float index_scale;
+    int32_t index_topk;         /* 1 .. DSA_MAX_TOPK */
+    int32_t window;             /* >= 0 */
+    /* attention */
+    const void* q;              /* [B, 1, Hq, Dqk] bf16 */
+    const void* kv;             /* [B, S_max, Dqk] bf16 */
+    const float* attn_sink;     /* [Hq] fp32 or NULL */
+    int32_t Hq, Dqk, Dv;
+    float sm_scale;
+    /* outputs */
+    void* out;                  /* [B, 1, Hq, Dv] bf16 */
+    float* lse;                 /* [B, 1, Hq] fp32 or NULL */
+    float* scores;              /* [B, S_max] fp32 or NULL (then kept in workspace) */
+    int32_t* index_list;        /* [B, index_topk + window] int32 or NULL (then workspace) */
+} dsa_decode_args_t;
+
+size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args);
+dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

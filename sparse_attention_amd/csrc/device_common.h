@@ -1,0 +1,77 @@
+// Device helpers shared by the gfx950 kernels of libdsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Most negative finite bfloat16 (0xFF7F), exact in fp32: the finite mask
+// bound of slots a row cannot attend to.
+__host__ __device__ __forceinline__ float mask_bound() { return -0x1.FEp+127f; }
+
+// Attendable slots of row r (positions+1, capped by valid_len, clamped).
+__device__ __forceinline__ int n_valid_of(const int32_t* positions, int32_t valid_len, int32_t r, int32_t S_max)
+{
+    long long n = positions ? (long long)positions[r] + 1 : (long long)S_max;
+    if (valid_len >= 0 && (long long)valid_len < n) n = valid_len;
+    if (n < 0) n = 0;
+    if (n > S_max) n = S_max;
+    return (int)n;
+}
+
+// The two bfloat16 halves of a 32-bit word as fp32 (low half = lower address).
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// fp32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// DPP lane exchanges inside a row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<DPP_QUAD_XOR1>(x);
+    x += dpp<DPP_QUAD_XOR2>(x);
+    x += dpp<DPP_ROW_HALF_MIRROR>(x);
+    x += dpp<DPP_ROW_MIRROR>(x);
+    return x;
+}
+// Sum over aligned groups of 8 lanes.
+__device__ __forceinline__ float row8_sum(float x)
+{
+    x += dpp<DPP_QUAD_XOR1>(x);
+    x += dpp<DPP_QUAD_XOR2>(x);
+    x += dpp<DPP_ROW_HALF_MIRROR>(x);
+    return x;
+}
+
+// Order-preserving map of a (non-NaN) fp32 to uint32: a < b  <=>  key(a) < key(b).
+__device__ __forceinline__ uint32_t f32_order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

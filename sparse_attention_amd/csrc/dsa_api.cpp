@@ -1,0 +1,225 @@
+// C entry points of libdsa: host-side validation, workspace carving and
+// dispatch to the gfx950 kernels.  Validation completes before anything is
+// enqueued, so an error status leaves every output untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+dsa_status_t launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+dsa_status_t check_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                               dsa_key_dtype_t k_dtype, int32_t M, int32_t rows_per_seq, int32_t H, int32_t D,
+                               int32_t S_max, uint32_t flags, const float* scores)
+{
+    if (!q || !w || !k_cache || !scores) return DSA_ERR_NULL;
+    if (k_dtype != DSA_KEY_BF16 && k_dtype != DSA_KEY_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+    if (k_dtype == DSA_KEY_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+    if (k_dtype == DSA_KEY_BF16 && k_scale) return DSA_ERR_SHAPE;
+    if (M < 1 || rows_per_seq < 1 || H < 1 || S_max < 1) return DSA_ERR_SHAPE;
+    if (M % rows_per_seq != 0) return DSA_ERR_SHAPE;
+    if (D != DSA_INDEX_HEAD_DIM) return DSA_ERR_UNSUPPORTED;
+    if (H > 128) return DSA_ERR_UNSUPPORTED;
+    if (flags & ~DSA_SCORE_RELU) return DSA_ERR_UNSUPPORTED;
+    if (rows_per_seq == 1) {
+        if (flags != 0) return DSA_ERR_UNSUPPORTED;  // decode scoring folds heads: identity only
+        if (M > 65535) return DSA_ERR_SHAPE;
+    } else {
+        if (k_dtype != DSA_KEY_BF16 || H > 64) return DSA_ERR_UNSUPPORTED;
+        if (!dsa::score_prefill_available()) return DSA_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(q) || !aligned16(k_cache)) return DSA_ERR_ALIGN;
+    if (!aligned16(w) || !aligned16(scores) || (k_scale && !aligned16(k_scale))) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+dsa_status_t check_topk(const float* scores, int32_t M, int32_t S_max, int32_t k, const int32_t* topk_idx)
+{
+    if (!scores || !topk_idx) return DSA_ERR_NULL;
+    if (M < 1 || S_max < 1) return DSA_ERR_SHAPE;
+    if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+    if (!aligned16(scores) || !aligned16(topk_idx)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t B, int32_t S, int32_t Hq,
+                               int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, const void* out)
+{
+    if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
+    if (B < 1 || S < 1 || Hq < 1 || S_kv < 1 || K_top < 1) return DSA_ERR_SHAPE;
+    if (Dqk < 32 || Dqk > DSA_MAX_ATTN_DIM || Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
+    if (Dv < 16 || Dv > Dqk || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
+    if ((long long)B * S > 65535) return DSA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+struct decode_layout {
+    size_t scores_off, scores_bytes;
+    size_t list_off, list_bytes;
+    size_t attn_off, attn_bytes;
+    size_t total;
+};
+
+decode_layout layout_decode(const dsa_decode_args_t* a)
+{
+    decode_layout L{};
+    size_t off = 0;
+    L.scores_bytes = a->scores ? 0 : (size_t)a->B * a->S_max * sizeof(float);
+    L.scores_off = off;
+    off += round_up(L.scores_bytes);
+    const int32_t K_top = a->index_topk + a->window;
+    L.list_bytes = a->index_list ? 0 : (size_t)a->B * K_top * sizeof(int32_t);
+    L.list_off = off;
+    off += round_up(L.list_bytes);
+    L.attn_bytes = dsa::sparse_attn_partial_bytes(a->B, 1, a->Hq, a->Dv, K_top);
+    L.attn_off = off;
+    off += round_up(L.attn_bytes);
+    L.total = off;
+    return L;
+}
+
+dsa_status_t check_decode(const dsa_decode_args_t* a)
+{
+    if (!a) return DSA_ERR_NULL;
+    if (a->struct_size < sizeof(dsa_decode_args_t)) return DSA_ERR_UNSUPPORTED;
+    if (!a->index_q || !a->index_w || !a->k_cache || !a->q || !a->kv || !a->out) return DSA_ERR_NULL;
+    if (a->k_dtype != DSA_KEY_BF16 && a->k_dtype != DSA_KEY_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+    if (a->k_dtype == DSA_KEY_FP8_E4M3 && !a->k_scale) return DSA_ERR_NULL;
+    if (a->k_dtype == DSA_KEY_BF16 && a->k_scale) return DSA_ERR_SHAPE;
+    if (a->B < 1 || a->B > 65535 || a->H < 1 || a->S_max < 1) return DSA_ERR_SHAPE;
+    if (a->H > 128) return DSA_ERR_UNSUPPORTED;
+    if (a->index_topk < 1 || a->index_topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+    if (a->window < 0 || a->window > a->S_max) return DSA_ERR_SHAPE;
+    if (a->Hq < 1) return DSA_ERR_SHAPE;
+    if (a->Dqk < 32 || a->Dqk > DSA_MAX_ATTN_DIM || a->Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
+    if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
+    if (!aligned16(a->index_q) || !aligned16(a->index_w) || !aligned16(a->k_cache) || !aligned16(a->q) ||
+        !aligned16(a->kv) || !aligned16(a->out))
+        return DSA_ERR_ALIGN;
+    if ((a->k_scale && !aligned16(a->k_scale)) || (a->scores && !aligned16(a->scores)) ||
+        (a->index_list && !aligned16(a->index_list)))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_version(void) { return "0.1.0"; }
+
+const char* dsa_status_string(dsa_status_t status)
+{
+    switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a size is out of range or inconsistent";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: request not implemented by this build";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: kernel launch failed";
+    }
+    return "unknown dsa_status_t";
+}
+
+float dsa_mask_bound(void) { return -0x1.FEp+127f; }
+
+dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                             dsa_key_dtype_t k_dtype, const int32_t* positions, int32_t valid_len, int32_t M,
+                             int32_t rows_per_seq, int32_t H, int32_t D, int32_t S_max, float scale,
+                             uint32_t flags, float* scores, hipStream_t stream)
+{
+    dsa_status_t s = check_index_score(q, w, k_cache, k_scale, k_dtype, M, rows_per_seq, H, D, S_max, flags, scores);
+    if (s != DSA_OK) return s;
+    if (rows_per_seq == 1)
+        return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
+                                                      valid_len, M, H, S_max, scale, scores, stream));
+    return launch_status(dsa::launch_score_prefill(q, w, k_cache, positions, valid_len, M, rows_per_seq, H, S_max,
+                                                   scale, (flags & DSA_SCORE_RELU) != 0, scores, stream));
+}
+
+size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk)
+{
+    (void)M;
+    (void)S_max;
+    (void)index_topk;
+    return 0;
+}
+
+dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions, int32_t valid_len,
+                      int32_t index_topk, int32_t* topk_idx, float* topk_scores, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream)
+{
+    dsa_status_t s = check_topk(scores, M, S_max, index_topk, topk_idx);
+    if (s != DSA_OK) return s;
+    if (workspace_bytes < dsa_topk_workspace_size(M, S_max, index_topk)) return DSA_ERR_WORKSPACE;
+    (void)workspace;
+    return launch_status(
+        dsa::launch_topk(scores, M, S_max, positions, valid_len, index_topk, 0, topk_idx, topk_scores, stream));
+}
+
+size_t dsa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
+{
+    if (B < 1 || S < 1 || Hq < 1 || Dv < 1 || K_top < 1) return 0;
+    return dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+}
+
+dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idx, int32_t B,
+                             int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top,
+                             float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    dsa_status_t s = check_sparse_attn(q, kv, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, out);
+    if (s != DSA_OK) return s;
+    const size_t need = dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    return launch_status(dsa::launch_sparse_attn(q, kv, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale,
+                                                 out, lse, workspace, stream));
+}
+
+size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args)
+{
+    if (!args || args->struct_size < sizeof(dsa_decode_args_t) || args->B < 1 || args->S_max < 1 ||
+        args->index_topk < 1 || args->window < 0 || args->Hq < 1 || args->Dv < 1)
+        return 0;
+    return layout_decode(args).total;
+}
+
+dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    dsa_status_t s = check_decode(args);
+    if (s != DSA_OK) return s;
+    const decode_layout L = layout_decode(args);
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return DSA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    float* scores = args->scores ? args->scores : reinterpret_cast<float*>(ws + L.scores_off);
+    int32_t* list = args->index_list ? args->index_list : reinterpret_cast<int32_t*>(ws + L.list_off);
+    void* attn_ws = L.attn_bytes ? static_cast<void*>(ws + L.attn_off) : nullptr;
+    const int32_t K_top = args->index_topk + args->window;
+
+    hipError_t e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
+                                            args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
+                                            args->B, args->H, args->S_max, args->index_scale, scores, stream);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
+                         args->window, list, nullptr, stream);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
+                                args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);
+    return launch_status(e);
+}
+
+}  // extern "C"

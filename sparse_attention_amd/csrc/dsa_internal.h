@@ -1,0 +1,41 @@
+// Internal launcher interface of libdsa (host side).  Each launcher assumes
+// its arguments were validated by the C entry points and only enqueues
+// kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Decode indexer score, one row per sequence (phi = identity).
+hipError_t launch_score_decode(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                               bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
+                               int32_t H, int32_t S_max, float scale, float* scores, hipStream_t stream);
+
+// Whether this build contains the prefill (per-head MFMA) scoring kernel.
+bool score_prefill_available();
+
+// Prefill indexer score: rows_per_seq query rows share one bf16 cache; per-head MFMA.
+hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cache, const int32_t* positions,
+                                int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,
+                                float scale, bool relu, float* scores, hipStream_t stream);
+
+// Top-k per row.  With window > 0 the output row has width k + window and
+// holds the top-k with in-window entries replaced by -1, followed by the
+// window positions (the decode-step index list).
+hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
+                       int32_t valid_len, int32_t k, int32_t window, int32_t* out_idx, float* out_scores,
+                       hipStream_t stream);
+
+// Split count and partial-buffer size of the sparse attention launch.
+int sparse_attn_splits(int32_t B, int32_t S, int32_t Hq, int32_t K_top);
+size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
+
+hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
+                              int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
+                              int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
+                              hipStream_t stream);
+
+}  // namespace dsa

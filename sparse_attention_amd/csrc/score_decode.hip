@@ -1,0 +1,254 @@
+// Decode lightning-indexer score (one query row per sequence) for gfx950.
+//
+// Definition (AWS Neuron "DeepSeek-V3.2 Sparse Indexer Kernel API
+// Reference", Returns and Notes): every cached key slot s of row r gets
+//   score = scale * sum_h w[r,h] * (q[r,h,:] . K[r,s,:])
+// and slots the row cannot attend to get the finite mask bound.
+//
+// With the identity activation the head sum folds by linearity into one
+// fp32 query, q_eff[d] = scale * sum_h w[r,h] q[r,h,d], so each slot costs
+// one 128-long dot product: 0.5 flop per key byte, far below the HBM ridge.
+// The kernel is therefore a coalesced streaming read of the key cache:
+//   - grid (chunks of 512 slots, rows); chunks past n_valid only write the
+//     mask bound, so the dispatcher balances rows of different lengths;
+//   - bf16 keys: 16 lanes x 16 B cover one 256-B slot, a wave load moves
+//     4 consecutive slots (1 KiB); fp8 keys: 8 lanes x 16 B per 128-B slot;
+//   - the first key loads are issued before the fold so their latency
+//     overlaps it; loads are double-buffered in registers;
+//   - partial dots are summed across the lanes of a slot with DPP row ops.
+#include "device_common.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 512;   // slots per workgroup
+constexpr int kUnroll = 8;    // loads in flight per lane per buffer
+
+// q_eff[d] = scale * sum_h w[h] q[h][d] into LDS (256 threads: 16 head
+// groups x 16 blocks of 8 dims).
+__device__ __forceinline__ void fold_query(const uint16_t* __restrict__ q, const float* __restrict__ w, int H,
+                                           float scale, float* red, float* qe)
+{
+    const int t = threadIdx.x;
+    const int dblk = t & 15;
+    const int hg = t >> 4;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int h = hg; h < H; h += 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(q + (size_t)h * 128 + dblk * 8);
+        const float wh = w[h];
+        acc[0] = fmaf(wh, bf16_lo(v.x), acc[0]);
+        acc[1] = fmaf(wh, bf16_hi(v.x), acc[1]);
+        acc[2] = fmaf(wh, bf16_lo(v.y), acc[2]);
+        acc[3] = fmaf(wh, bf16_hi(v.y), acc[3]);
+        acc[4] = fmaf(wh, bf16_lo(v.z), acc[4]);
+        acc[5] = fmaf(wh, bf16_hi(v.z), acc[5]);
+        acc[6] = fmaf(wh, bf16_lo(v.w), acc[6]);
+        acc[7] = fmaf(wh, bf16_hi(v.w), acc[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[hg * 128 + dblk * 8 + i] = acc[i];
+    __syncthreads();
+    if (t < 128) {
+        float s = 0.f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) s += red[g * 128 + t];
+        qe[t] = s * scale;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ float dot8_bf16(const float* qv, u32x4 v)
+{
+    float p = qv[0] * bf16_lo(v.x);
+    p = fmaf(qv[1], bf16_hi(v.x), p);
+    p = fmaf(qv[2], bf16_lo(v.y), p);
+    p = fmaf(qv[3], bf16_hi(v.y), p);
+    p = fmaf(qv[4], bf16_lo(v.z), p);
+    p = fmaf(qv[5], bf16_hi(v.z), p);
+    p = fmaf(qv[6], bf16_lo(v.w), p);
+    p = fmaf(qv[7], bf16_hi(v.w), p);
+    return p;
+}
+
+// bf16 keys: slot = 256 B = 16 lanes x 16 B.  Per wave and buffer:
+// kUnroll x 4 consecutive slots.
+__global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ positions, int32_t valid_len, int32_t H, int32_t S_max, float scale,
+    float* __restrict__ scores)
+{
+    __shared__ float red[16 * 128];
+    __shared__ float qe[128];
+    const int r = blockIdx.y;
+    const int s0 = blockIdx.x * kChunk;
+    const int s1 = min(s0 + kChunk, S_max);
+    const int nv = n_valid_of(positions, valid_len, r, S_max);
+    float* __restrict__ out = scores + (size_t)r * S_max;
+
+    const float mb = mask_bound();
+    for (int s = max(s0, nv) + (int)threadIdx.x; s < s1; s += kThreads) out[s] = mb;
+    const int se = min(s1, nv);
+    if (s0 >= se) return;  // uniform over the workgroup
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;      // slot within a group of 4
+    const int dblk = lane & 15;   // dims 8*dblk .. 8*dblk+7
+    const uint16_t* __restrict__ kr = k + (size_t)r * S_max * 128 + dblk * 8;
+    constexpr int kWaveSlots = 4 * kUnroll;
+    constexpr int kIterSlots = 4 * kWaveSlots;
+
+    u32x4 buf[kUnroll];
+    int base = s0 + wave * kWaveSlots;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int s = base + 4 * u + g;
+        buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
+                          : u32x4{0, 0, 0, 0};
+    }
+
+    fold_query(q + (size_t)r * H * 128, w + (size_t)r * H, H, scale, red, qe);
+    float qv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = qe[dblk * 8 + i];
+
+    for (; base < se; base += kIterSlots) {
+        u32x4 cur[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
+        const int nb = base + kIterSlots;
+        if (nb < se) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int s = nb + 4 * u + g;
+                buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
+                                  : u32x4{0, 0, 0, 0};
+            }
+        }
+        float part[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) part[u] = row16_sum(dot8_bf16(qv, cur[u]));
+        // lane (g, j) writes slot base + 4j + g for j < kUnroll
+        float val = part[0];
+#pragma unroll
+        for (int u = 1; u < kUnroll; ++u) val = (dblk == u) ? part[u] : val;
+        const int s = base + 4 * dblk + g;
+        if (dblk < kUnroll && s < se) out[s] = val;
+    }
+}
+
+// fp8 keys: slot = 128 B codes + one fp32 scale; 8 lanes x 16 B per slot,
+// a wave load moves 8 consecutive slots.
+__device__ __forceinline__ float dot16_fp8(const float* qv, u32x4 v)
+{
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    float p = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);
+        p = fmaf(qv[4 * i + 0], a[0], p);
+        p = fmaf(qv[4 * i + 1], a[1], p);
+        p = fmaf(qv[4 * i + 2], b[0], p);
+        p = fmaf(qv[4 * i + 3], b[1], p);
+    }
+    return p;
+}
+
+__global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ positions, int32_t valid_len, int32_t H,
+    int32_t S_max, float scale, float* __restrict__ scores)
+{
+    __shared__ float red[16 * 128];
+    __shared__ float qe[128];
+    const int r = blockIdx.y;
+    const int s0 = blockIdx.x * kChunk;
+    const int s1 = min(s0 + kChunk, S_max);
+    const int nv = n_valid_of(positions, valid_len, r, S_max);
+    float* __restrict__ out = scores + (size_t)r * S_max;
+
+    const float mb = mask_bound();
+    for (int s = max(s0, nv) + (int)threadIdx.x; s < s1; s += kThreads) out[s] = mb;
+    const int se = min(s1, nv);
+    if (s0 >= se) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 3;     // slot within a group of 8
+    const int dblk = lane & 7;   // dims 16*dblk .. 16*dblk+15
+    const uint8_t* __restrict__ kr = k + (size_t)r * S_max * 128 + dblk * 16;
+    const float* __restrict__ ksr = k_scale + (size_t)r * S_max;
+    constexpr int kWaveSlots = 8 * kUnroll;
+    constexpr int kIterSlots = 4 * kWaveSlots;
+
+    u32x4 buf[kUnroll];
+    float sbuf;
+    int base = s0 + wave * kWaveSlots;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int s = base + 8 * u + g;
+        buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
+                          : u32x4{0, 0, 0, 0};
+    }
+    {
+        const int s = base + 8 * dblk + g;
+        sbuf = (s < se) ? ksr[s] : 0.f;
+    }
+
+    fold_query(q + (size_t)r * H * 128, w + (size_t)r * H, H, scale, red, qe);
+    float qv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = qe[dblk * 16 + i];
+
+    for (; base < se; base += kIterSlots) {
+        u32x4 cur[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
+        const float cs = sbuf;
+        const int nb = base + kIterSlots;
+        if (nb < se) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int s = nb + 8 * u + g;
+                buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
+                                  : u32x4{0, 0, 0, 0};
+            }
+            const int s = nb + 8 * dblk + g;
+            sbuf = (s < se) ? ksr[s] : 0.f;
+        }
+        float part[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) part[u] = row8_sum(dot16_fp8(qv, cur[u]));
+        float val = part[0];
+#pragma unroll
+        for (int u = 1; u < kUnroll; ++u) val = (dblk == u) ? part[u] : val;
+        const int s = base + 8 * dblk + g;
+        if (s < se) out[s] = val * cs;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_score_decode(const void* q, const float* w, const void* k_cache, const float* k_scale,
+                               bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
+                               int32_t H, int32_t S_max, float scale, float* scores, hipStream_t stream)
+{
+    const dim3 grid((S_max + kChunk - 1) / kChunk, M);
+    if (key_fp8) {
+        score_decode_fp8_kernel<<<grid, kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), k_scale, positions,
+            valid_len, H, S_max, scale, scores);
+    } else {
+        score_decode_bf16_kernel<<<grid, kThreads, 0, stream>>>(
+            static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k_cache), positions, valid_len, H,
+            S_max, scale, scores);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dsa

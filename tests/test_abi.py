@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every symbol include/dsa.h declares, and
+validates arguments on the host (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIB = os.path.join(ROOT, "sparse_attention_amd", "libdsa.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdsa.so is not built (run __graft_entry__.build())")
+    import sparse_attention_amd as m
+
+    return m.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("dsa_index_score", "dsa_topk", "dsa_sparse_attn", "dsa_decode_step"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_constants(lib):
+    assert lib.dsa_version().decode().count(".") == 2
+    mb = lib.dsa_mask_bound()
+    import struct
+    assert struct.unpack("<I", struct.pack("<f", mb))[0] == 0xFF7F0000
+    assert b"NULL" in lib.dsa_status_string(ERR_NULL)
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A = 0x10000  # a fake, aligned, non-null "device" address; never dereferenced on these paths
+
+
+def test_index_score_validation(lib):
+    f = lib.dsa_index_score
+    args = dict(q=_p(A), w=_p(A), k=_p(A), ks=None, kd=0, pos=None, vl=-1, M=2, rps=1, H=4, D=128, S=100,
+                scale=1.0, flags=0, out=_p(A))
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["w"], a["k"], a["ks"], a["kd"], a["pos"], a["vl"], a["M"], a["rps"], a["H"], a["D"],
+                 a["S"], a["scale"], a["flags"], a["out"], None)
+
+    assert call(q=None) == ERR_NULL
+    assert call(out=None) == ERR_NULL
+    assert call(kd=1) == ERR_NULL                 # fp8 without scales
+    assert call(ks=_p(A)) == ERR_SHAPE            # bf16 with scales
+    assert call(D=64) == ERR_UNSUPPORTED
+    assert call(H=0) == ERR_SHAPE
+    assert call(H=129) == ERR_UNSUPPORTED
+    assert call(M=3, rps=2) == ERR_SHAPE
+    assert call(flags=1) == ERR_UNSUPPORTED       # relu on the folded decode path
+    assert call(flags=4) == ERR_UNSUPPORTED
+    assert call(q=_p(A + 8)) == ERR_ALIGN
+    assert call(kd=7) == ERR_UNSUPPORTED
+
+
+def test_topk_validation(lib):
+    f = lib.dsa_topk
+    assert f(None, 1, 10, None, -1, 4, _p(A), None, None, 0, None) == ERR_NULL
+    assert f(_p(A), 0, 10, None, -1, 4, _p(A), None, None, 0, None) == ERR_SHAPE
+    assert f(_p(A), 1, 10, None, -1, 0, _p(A), None, None, 0, None) == ERR_UNSUPPORTED
+    assert f(_p(A), 1, 10, None, -1, 2049, _p(A), None, None, 0, None) == ERR_UNSUPPORTED
+    assert lib.dsa_topk_workspace_size(16, 32768, 1024) == 0
+
+
+def test_sparse_attn_validation_and_workspace(lib):
+    f = lib.dsa_sparse_attn
+
+    def call(B=2, S=1, Hq=128, Dqk=576, Dv=512, S_kv=1000, K=1152, ws=None, nws=0, q=_p(A)):
+        return f(q, _p(A), None, _p(A), B, S, Hq, Dqk, Dv, S_kv, K, 0.1, _p(A), None, ws, nws, None)
+
+    assert call(q=None) == ERR_NULL
+    assert call(Dqk=600) == ERR_UNSUPPORTED
+    assert call(Dqk=100) == ERR_UNSUPPORTED
+    assert call(Dv=600) == ERR_UNSUPPORTED
+    assert call(Dv=24) == ERR_UNSUPPORTED
+    assert call(K=0) == ERR_SHAPE
+    need = lib.dsa_sparse_attn_workspace_size(2, 1, 128, 512, 1152)
+    assert need > 0
+    assert call() == ERR_WORKSPACE
+    assert call(ws=_p(A), nws=need - 1) == ERR_WORKSPACE
+    # one (token, head group) per split would already fill the chip: no workspace
+    assert lib.dsa_sparse_attn_workspace_size(1024, 1, 64, 512, 64) == 0
+
+
+def test_decode_step_validation(lib):
+    import sparse_attention_amd as m
+
+    a = m._DecodeArgs()
+    a.struct_size = ctypes.sizeof(m._DecodeArgs)
+    for name in ("index_q", "index_w", "k_cache", "q", "kv", "out"):
+        setattr(a, name, A)
+    a.B, a.H, a.S_max, a.index_topk, a.window = 4, 64, 4096, 1024, 128
+    a.Hq, a.Dqk, a.Dv, a.valid_len = 128, 576, 512, -1
+    ws = lib.dsa_decode_step_workspace_size(ctypes.byref(a))
+    assert ws >= 4 * 4096 * 4 + 4 * 1152 * 4
+    assert lib.dsa_decode_step(ctypes.byref(a), None, 0, None) == ERR_WORKSPACE
+    a.window = -1
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE
+    a.window = 128
+    a.q = None
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_NULL
+    a.q = A
+    a.struct_size = 8
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED

@@ -1,0 +1,253 @@
+"""GPU parity of each entry point against the CPU oracle on seeded inputs (needs an MI355X).
+
+Sizes are small enough for the oracle to finish in seconds while spanning
+several workgroup tiles and ragged tails; the edge matrix covers empty and
+ragged rows, k around n_valid, masked / out-of-range / duplicate indices,
+sinks of either sign and no sink.  Full-size workloads are in
+test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from parity import (check_attn, check_scores, check_topk_own_scores, check_topk_same_scores, n_valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print("\n[gpu case] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_amd as m
+
+    m.load_library()
+    assert torch.cuda.is_available(), "no GPU visible"
+    return m
+
+
+def _cuda(t):
+    return None if t is None else t.contiguous().cuda()
+
+
+# ------------------------------------------------------------------ scores
+
+def _score_case(dsa, w, label):
+    announce("dsa_index_score %s M=%d S_max=%d H=%d fp8=%s" % (label, w.M, w.S_max, w.index_q.shape[1], w.key_fp8))
+    got = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                              k_scale=_cuda(w.k_scale), positions=_cuda(w.positions), valid_len=w.valid_len,
+                              rows_per_seq=w.rows_per_seq)
+    torch.cuda.synchronize()
+    ref = oracle.index_score(w.index_q, w.index_w, w.k_cache, k_scale=w.k_scale, scale=w.index_scale,
+                             positions=w.positions, valid_len=w.valid_len, rows_per_seq=w.rows_per_seq)
+    nv = n_valid_rows(None if w.positions is None else w.positions.numpy(), w.valid_len, w.M, w.S_max)
+    return check_scores(got.cpu().numpy(), ref, nv, oracle.mask_bound())
+
+
+def test_score_tiny_decode(dsa):
+    _score_case(dsa, synthetic.make_workload("tiny_decode"), "tiny_decode")
+
+
+@pytest.mark.parametrize("H", [1, 4, 64, 128])
+def test_score_decode_bf16_edges(dsa, H):
+    S_max = 5000  # not a multiple of the 512-slot chunk
+    w = synthetic.make_workload("batched_decode", M=9, H=H, S_max=S_max, pos_lo=0, topk=64)
+    w.positions = torch.tensor([-1, 0, 62, 63, 64, 511, 512, S_max - 2, S_max - 1], dtype=torch.int32)
+    _score_case(dsa, w, "edges H=%d" % H)
+
+
+def test_score_decode_valid_len_cap(dsa):
+    w = synthetic.make_workload("batched_decode", M=4, S_max=3000, pos_lo=100, topk=64)
+    w.valid_len = 1234
+    _score_case(dsa, w, "valid_len cap")
+    w.positions = None
+    _score_case(dsa, w, "valid_len only")
+
+
+def test_score_decode_fp8(dsa):
+    w = synthetic.make_workload("fp8_long_decode", M=3, S_max=3000, vl_lo=1000, topk=64)
+    _score_case(dsa, w, "fp8 scaled")
+
+
+def test_score_decode_fp8_all_codes(dsa):
+    """Every finite E4M3 code, one-hot queries: scores = value(code) * scale exactly decoded."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]          # 254 finite codes
+    S_max = 256
+    kc = np.zeros((1, S_max, 128), np.uint8)
+    kc[0, : len(codes), 5] = codes
+    kc[0, : len(codes), 77] = codes[::-1]
+    w = synthetic.make_workload("fp8_long_decode", M=1, S_max=S_max, vl_lo=S_max, topk=8)
+    w.k_cache = torch.from_numpy(kc)
+    w.k_scale = torch.full((1, S_max), 0.5, dtype=torch.float32)
+    w.positions = torch.tensor([S_max - 1], dtype=torch.int32)
+    _score_case(dsa, w, "fp8 all codes")
+
+
+# ------------------------------------------------------------------ top-k
+
+@pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (70000, 2048), (3000, 2048)])
+def test_topk_edges(dsa, S_max, k):
+    g = np.random.default_rng(S_max * 7 + k)
+    nvs = sorted({0, 1, max(0, k - 1), k, k + 1, S_max // 2, S_max - 1, S_max})
+    nvs = [n for n in nvs if 0 <= n <= S_max]
+    M = len(nvs)
+    sc = g.standard_normal((M, S_max)).astype(np.float32)
+    sc[1::2] = np.round(sc[1::2] * 4) / 4  # heavy exact ties on odd rows
+    sc[:, ::97] = 1e30                      # large values, also beyond n_valid
+    pos = np.array(nvs, np.int32) - 1
+    announce("dsa_topk S_max=%d k=%d rows=%d" % (S_max, k, M))
+    idx, tsc = dsa.dsa_topk(torch.from_numpy(sc).cuda(), k, positions=torch.from_numpy(pos).cuda(), with_scores=True)
+    torch.cuda.synchronize()
+    idx, tsc = idx.cpu().numpy(), tsc.cpu().numpy()
+    nv = np.array(nvs)
+    check_topk_same_scores(idx, sc, nv, k)
+    for i in range(M):
+        ok = idx[i] >= 0
+        assert np.array_equal(tsc[i][ok], sc[i, idx[i][ok]])
+        assert np.all(np.isneginf(tsc[i][~ok]))
+
+
+def test_topk_all_equal_row(dsa):
+    sc = np.zeros((2, 4000), np.float32)
+    announce("dsa_topk all-equal rows")
+    idx = dsa.dsa_topk(torch.from_numpy(sc).cuda(), 1000, valid_len=3999).cpu().numpy()
+    check_topk_same_scores(idx, sc, np.array([3999, 3999]), 1000)
+
+
+# ------------------------------------------------------------------ sparse attention
+
+def _attn_inputs(seed, B, S, Hq, Dqk, Dv, S_kv, K_top, masked=0.1, dup=0.0, oob=0.0, sink="normal"):
+    g = np.random.default_rng(seed)
+    q = torch.from_numpy(g.standard_normal((B, S, Hq, Dqk)).astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy((g.standard_normal((B, S_kv, Dqk)) * 0.5).astype(np.float32)).to(torch.bfloat16)
+    idx = np.stack([np.stack([g.choice(S_kv, size=K_top, replace=K_top > S_kv) for _ in range(S)])
+                    for _ in range(B)]).astype(np.int32)
+    r = g.random(idx.shape)
+    idx[r < masked] = -1
+    idx[(r >= masked) & (r < masked + oob)] = S_kv + 5
+    if dup > 0:
+        d = g.random(idx.shape) < dup
+        idx[d] = idx[..., :1].repeat(idx.shape[-1], -1)[d]
+    if sink == "normal":
+        sk = torch.from_numpy(g.standard_normal(Hq).astype(np.float32))
+    elif sink is None:
+        sk = None
+    else:
+        sk = torch.full((Hq,), float(sink), dtype=torch.float32)
+    return q, kv, sk, torch.from_numpy(idx)
+
+
+def _attn_case(dsa, label, q, kv, sk, idx, sm_scale, Dv):
+    B, S, Hq, Dqk = q.shape
+    announce("dsa_sparse_attn %s B=%d S=%d Hq=%d Dqk=%d Dv=%d S_kv=%d K_top=%d" % (
+        label, B, S, Hq, Dqk, Dv, kv.shape[1], idx.shape[2]))
+    out, lse = dsa.dsa_sparse_attn(_cuda(q), _cuda(kv), _cuda(sk), _cuda(idx), sm_scale=sm_scale, dv=Dv,
+                                   with_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.sparse_attn(q, kv, sk, idx, sm_scale=sm_scale, dv=Dv)
+    err, rel = check_attn(out.float().cpu().numpy(), ref)
+    g_lse = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(g_lse), fin)
+    np.testing.assert_allclose(g_lse[fin], ref_lse[fin], rtol=1e-4, atol=1e-4)
+    return err, rel
+
+
+def test_attn_tiny_decode_shape(dsa):
+    q, kv, sk, idx = _attn_inputs(1, 1, 1, 8, 192, 128, 2048, 64)
+    _attn_case(dsa, "tiny", q, kv, sk, idx, 192 ** -0.5, 128)
+
+
+def test_attn_full_decode_shape_split(dsa):
+    q, kv, sk, idx = _attn_inputs(2, 2, 1, 128, 576, 512, 3000, 1152, masked=0.05)
+    _, rel = _attn_case(dsa, "mla-shaped split", q, kv, sk, idx, 576 ** -0.5, 512)
+    assert rel < 2e-2
+
+
+@pytest.mark.parametrize("K_top", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("sink", [None, -30.0, 0.0, 30.0])
+def test_attn_ktop_and_sink(dsa, K_top, sink):
+    q, kv, sk, idx = _attn_inputs(3 + K_top, 2, 2, 16, 64, 64, 500, K_top, masked=0.2, sink=sink)
+    _attn_case(dsa, "K_top=%d sink=%s" % (K_top, sink), q, kv, sk, idx, 0.125, 64)
+
+
+def test_attn_index_patterns(dsa):
+    q, kv, sk, idx = _attn_inputs(4, 3, 2, 24, 128, 96, 700, 300, masked=0.1, dup=0.1, oob=0.05)
+    idx[0, 0, :] = -1                 # all masked
+    idx[0, 1, :100] = -1              # leading -1
+    idx[1, 0, -150:] = -1             # trailing -1
+    idx[2, 1, :] = 699                # one slot repeated
+    _attn_case(dsa, "index patterns", q, kv, sk, idx, 0.1, 96)
+    _attn_case(dsa, "index patterns no sink", q, kv, None, idx, 0.1, 96)
+
+
+def test_attn_peaked_softmax(dsa):
+    q, kv, sk, idx = _attn_inputs(5, 2, 1, 64, 576, 512, 2000, 512)
+    q = (q.float() * 8).to(torch.bfloat16)
+    _, rel = _attn_case(dsa, "peaked", q, kv, sk, idx, 576 ** -0.5, 512)
+    assert rel < 2e-2
+
+
+# ------------------------------------------------------------------ decode step
+
+def _decode_case(dsa, w, label):
+    announce("dsa_decode_step %s B=%d S_max=%d topk=%d window=%d Hq=%d Dqk=%d" % (
+        label, w.M, w.S_max, w.index_topk, w.window, w.q.shape[2], w.q.shape[3]))
+    step = dsa.dsa_decode_step(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), k_scale=_cuda(w.k_scale),
+                               positions=_cuda(w.positions), valid_len=w.valid_len, index_scale=w.index_scale,
+                               index_topk=w.index_topk, window=w.window, q=_cuda(w.q), kv=_cuda(w.kv),
+                               attn_sink=_cuda(w.sink), sm_scale=w.sm_scale, dv=w.dv)
+    torch.cuda.synchronize()
+    pos = None if w.positions is None else w.positions.numpy()
+    nv = n_valid_rows(pos, w.valid_len, w.M, w.S_max)
+    ref_sc = oracle.index_score(w.index_q, w.index_w, w.k_cache, k_scale=w.k_scale, scale=w.index_scale,
+                                positions=w.positions, valid_len=w.valid_len)
+    check_scores(step.scores.cpu().numpy(), ref_sc, nv, oracle.mask_bound())
+    ref_top = oracle.topk(ref_sc, w.index_topk, positions=w.positions, valid_len=w.valid_len)
+    ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=w.positions,
+                               valid_len=w.valid_len)
+    lst = step.index_list.cpu().numpy()
+    k = w.index_topk
+    assert np.array_equal(lst[:, k:], ref_list[:, k:]), "window part differs"
+    # top-k part: same set as the oracle's top-k up to the tie band, minus the window
+    for b in range(w.M):
+        wstart = int(nv[b]) - w.window
+        gtop = lst[b, :k]
+        assert np.all((gtop < 0) | (gtop < wstart))
+        G = set(lst[b][lst[b] >= 0].tolist())
+        R = set(ref_list[b][ref_list[b] >= 0].tolist())
+        assert len(G) == int((lst[b] >= 0).sum()), "duplicate in the GPU index list"
+        if G != R:  # allowed only inside the score tie band at the k-th boundary
+            o = ref_sc[b, : nv[b]].astype(np.float64)
+            vk = np.sort(o)[::-1][min(k, nv[b]) - 1]
+            tau = 1e-3 * max(abs(vk), float(np.sqrt(np.mean(o * o))))
+            assert all(o[s] >= vk - tau for s in G - R) and all(o[s] <= vk + tau for s in R - G)
+    ref_out, _ = oracle.sparse_attn(w.q, w.kv, w.sink, ref_list[:, None, :], sm_scale=w.sm_scale, dv=w.dv)
+    err, rel = check_attn(step.out.float().cpu().numpy(), ref_out)
+    return step, ref_sc, ref_list
+
+
+def test_decode_step_tiny(dsa):
+    _decode_case(dsa, synthetic.make_workload("tiny_decode"), "tiny_decode")
+
+
+def test_decode_step_mla_scaled(dsa):
+    w = synthetic.make_workload("full_decode_step", B=3, S_max=3000, topk=256, window=128)
+    w.positions = torch.tensor([2999, 100, 1500], dtype=torch.int32)
+    _decode_case(dsa, w, "scaled full step")
+
+
+def test_decode_step_fp8_keys(dsa):
+    w = synthetic.make_workload("full_decode_step", B=2, S_max=2000, topk=128, window=16, Hq=16, Dqk=192, Dv=128)
+    from synthetic.gen import quantize_fp8_blocks
+
+    codes, scales = quantize_fp8_blocks(w.k_cache.float())
+    w.k_cache, w.k_scale = codes, scales
+    _decode_case(dsa, w, "fp8 keys")
