@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA decode hot path on one MI355X.
+
+A step is one DSA decode step over a batch: lightning-indexer score of every
+cached key slot -> top-k -> index list (top-k plus the always-selected
+window) -> top-k sparse attention with sink (dsa_decode_step).  The default
+workload is the full decode step: 64 sequences x 65536 cached slots, indexer
+64 heads x 128, top-1024, window 128, attention 128 heads, qk 576 / v 512.
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+
+Prints ONE JSON line with the step throughput (attendable key slots scored
+per second through the whole step), per-kernel HIP-event timings, the
+roofline of the dominant kernel and the CPU oracle timed on a bounded sample
+of the same workload (which also re-checks parity on the timed buffers).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+METRIC = "DSA decode: indexer key-slots/s + sparse-attn tokens/s; % of HBM peak"
+PMC_FILE = os.path.join(ROOT, "profiles", "score_decode_full_decode_step.pmc.json")
+KERNEL_SOURCES = {"score_decode": "score_decode.hip", "topk": "topk.hip", "sparse_attn": "sparse_attn.hip"}
+
+
+def kernel_source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "sparse_attention_amd", "csrc", KERNEL_SOURCES[name])
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full_decode_step",
+                    choices=["full_decode_step", "tiny_decode", "batched_decode", "fp8_long_decode"])
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (scale reference for PMC byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def event_time_ms(torch, fn, iters):
+    """Average duration of fn() over iters launches, HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this DSA hot path is measured on exactly one GPU; --gpus %d (WORLD_SIZE %d) is not "
+              "supported. Sharding across GPUs is a design note only." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_amd as dsa
+    import synthetic
+
+    dsa.load_library()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = synthetic.make_workload(args.workload)
+    log("generated %s in %.1fs" % (args.workload, time.time() - t0))
+    c = lambda t: None if t is None else t.contiguous().to(dev)  # noqa: E731
+    gq, gw, gk, gks, gpos = c(w.index_q), c(w.index_w), c(w.k_cache), c(w.k_scale), c(w.positions)
+    has_attn = w.q is not None
+    if has_attn:
+        gaq, gkv, gsink = c(w.q), c(w.kv), c(w.sink)
+    torch.cuda.synchronize()
+    log("inputs resident on %s" % torch.cuda.get_device_name(0))
+
+    B, H, D = w.index_q.shape
+    S_max = w.S_max
+    nv = w.n_valid().numpy()
+    n_slots = int(nv.sum())
+    key_bytes_per_slot = D * (1 if w.key_fp8 else 2) + (4 if w.key_fp8 else 0)
+    score_bytes = n_slots * key_bytes_per_slot + B * S_max * 4 + B * H * D * 2 + B * H * 4
+    k = w.index_topk
+    K_top = k + w.window
+
+    if has_attn:
+        step = dsa.DecodeStep(gq, gw, gk, k_scale=gks, positions=gpos, valid_len=w.valid_len,
+                              index_scale=w.index_scale, index_topk=k, window=w.window, q=gaq, kv=gkv,
+                              attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv)
+        run_step = step
+    else:
+        scores_buf = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+
+        def run_step():
+            dsa.dsa_index_score(gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos,
+                                valid_len=w.valid_len, out=scores_buf)
+            return dsa.dsa_topk(scores_buf, k, positions=gpos, valid_len=w.valid_len)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ms_step = event_time_ms(torch, run_step, args.steps)
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
+    log("step %.3f ms (host wall %.3f ms/step)" % (ms_step, wall_ms))
+
+    # per-kernel timings (same inputs, same stream)
+    scores_t = step.scores if has_attn else scores_buf
+    kern = {}
+    ms_score = event_time_ms(torch, lambda: dsa.dsa_index_score(
+        gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos, valid_len=w.valid_len, out=scores_t),
+        args.steps)
+    kern["score_decode"] = {"us": ms_score * 1e3, "bytes": score_bytes,
+                            "GB/s": score_bytes / ms_score / 1e6,
+                            "hbm_frac": score_bytes / ms_score / 1e6 / HBM_PEAK_GBS,
+                            "key_slots_per_s": n_slots / ms_score * 1e3}
+    ms_topk = event_time_ms(torch, lambda: dsa.dsa_topk(scores_t, k, positions=gpos, valid_len=w.valid_len),
+                            args.steps)
+    topk_bytes = n_slots * 4 + B * k * 4
+    kern["topk"] = {"us": ms_topk * 1e3, "bytes": topk_bytes, "GB/s": topk_bytes / ms_topk / 1e6}
+    step_bytes = score_bytes + topk_bytes
+    if has_attn:
+        lst = step.index_list.view(B, 1, K_top)
+        n_entries = int((step.index_list >= 0).sum().item())
+        Hq, Dqk, Dv = w.q.shape[2], w.q.shape[3], w.dv
+        attn_bytes = n_entries * Dqk * 2 + B * Hq * Dqk * 2 + B * Hq * Dv * 2 + B * K_top * 4
+        attn_flops = 2.0 * Hq * n_entries * (Dqk + Dv)
+        ms_attn = event_time_ms(torch, lambda: dsa.dsa_sparse_attn(gaq, gkv, gsink, lst, sm_scale=w.sm_scale,
+                                                                  dv=Dv), args.steps)
+        kern["sparse_attn"] = {"us": ms_attn * 1e3, "bytes": attn_bytes, "flops": attn_flops,
+                               "GB/s": attn_bytes / ms_attn / 1e6,
+                               "hbm_frac": attn_bytes / ms_attn / 1e6 / HBM_PEAK_GBS,
+                               "mfma_frac": attn_flops / ms_attn / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                               "tokens_per_s": B / ms_attn * 1e3,
+                               "kv_entries_per_s": n_entries / ms_attn * 1e3}
+        step_bytes += attn_bytes
+    for name, v in kern.items():
+        log("%-12s %9.2f us  %8.1f GB/s" % (name, v["us"], v["GB/s"]))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies")
+        del src, dst
+
+    # dominant kernel roofline (HBM-bound streaming scorer)
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel") == dom and pmc.get("source_sha") == kernel_source_sha(dom) and \
+                pmc.get("workload") == args.workload:
+            traffic = pmc.get("hbm_bytes_per_launch")
+    if dom == "sparse_attn":
+        roof = {"bound": "mfma", "achieved": attn_flops / ms_attn / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+
+    # CPU oracle on a bounded sample of the same workload (+ parity on the timed buffers)
+    cpu = None
+    parity = None
+    if args.cpu_baseline == "on":
+        cpu, parity = cpu_baseline(args, w, step if has_attn else None, scores_t, nv, torch)
+
+    rec = {
+        "metric": METRIC,
+        "value": n_slots / ms_step * 1e3,
+        "unit": "key-slots/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "cache_slots": S_max, "attendable_slots": n_slots,
+                   "index_heads": H, "head_dim": D, "key_dtype": "fp8_e4m3" if w.key_fp8 else "bf16",
+                   "index_topk": k, "window": w.window,
+                   **({"attn_heads": int(w.q.shape[2]), "dqk": int(w.q.shape[3]), "dv": w.dv} if has_attn else {}),
+                   "parallelism": "single-gpu"},
+        "decode_tokens_per_s": B / ms_step * 1e3,
+        "step_hbm_frac": step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
+        "indexer_key_slots_per_s": kern["score_decode"]["key_slots_per_s"],
+        "sparse_attn_tokens_per_s": kern["sparse_attn"]["tokens_per_s"] if has_attn else None,
+        "kernels": kern,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, w, step, scores_t, nv, torch):
+    """Time the oracle (as it stands) on `cpu_sample` sequences of the same workload, and check the
+    GPU's outputs for those sequences against it."""
+    import oracle
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import check_attn, check_index_list, check_scores, check_topk_own_scores
+
+    ns = min(args.cpu_sample, w.M)
+    rows = np.linspace(0, w.M - 1, ns).round().astype(np.int64)
+    threads = oracle.default_threads()
+    threads = min(threads, 16)
+    pos = None if w.positions is None else w.positions[rows]
+    sub_k = w.k_cache[rows]
+    sub_ks = None if w.k_scale is None else w.k_scale[rows]
+    t0 = time.perf_counter()
+    ref_sc = oracle.index_score(w.index_q[rows], w.index_w[rows], sub_k, k_scale=sub_ks, scale=w.index_scale,
+                                positions=pos, valid_len=w.valid_len, nthreads=threads)
+    ref_top = oracle.topk(ref_sc, w.index_topk, positions=pos, valid_len=w.valid_len, nthreads=threads)
+    if step is not None:
+        ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=pos, valid_len=w.valid_len)
+        ref_out, _ = oracle.sparse_attn(w.q[rows], w.kv[rows], w.sink, ref_list[:, None, :], sm_scale=w.sm_scale,
+                                        dv=w.dv, nthreads=threads)
+    secs = time.perf_counter() - t0
+    n_slots = int(nv[rows].sum())
+    log("oracle: %d sequences in %.1fs on %d threads" % (ns, secs, threads))
+    parity = {}
+    check_scores(scores_t[torch.from_numpy(rows).to(scores_t.device)].cpu().numpy(), ref_sc, nv[rows],
+                 oracle.mask_bound())
+    parity["scores"] = "ok"
+    if step is None:
+        # the indexer-only workloads keep no top-k output: rerun it on the same scores
+        import sparse_attention_amd as dsa
+
+        got = dsa.dsa_topk(scores_t, w.index_topk, positions=None if w.positions is None else
+                           w.positions.to(scores_t.device), valid_len=w.valid_len).cpu().numpy()[rows]
+        check_topk_own_scores(got, ref_sc, nv[rows], w.index_topk)
+        parity["topk"] = "ok"
+    if step is not None:
+        check_index_list(step.index_list.cpu().numpy()[rows], ref_list, ref_sc, nv[rows], w.index_topk, w.window)
+        err, rel = check_attn(step.out.float().cpu().numpy()[rows], ref_out)
+        parity["index_list"] = "ok"
+        parity["attention_max_abs_err"] = err
+        parity["attention_max_rel_l2"] = rel
+    cpu = {"value": n_slots / secs, "unit": "key-slots/s", "cores": threads, "kind": "oracle",
+           "seconds": secs,
+           "sample": "%d of %d sequences (%d attendable slots): %s" % (
+               ns, w.M, n_slots, "score + full-sort top-k + window union + attention" if step is not None
+               else "score + full-sort top-k")}
+    if step is not None:
+        cpu["tokens_per_s"] = ns / secs
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

@@ -111,3 +111,27 @@ def check_attn(gpu_out: np.ndarray, ref_out: np.ndarray, atol: float = ATTN_ATOL
     num = np.sqrt((err ** 2).sum(axis=-1))
     den = np.maximum(np.sqrt((o ** 2).sum(axis=-1)), 1e-30)
     return float(err.max()), float((num / den).max())
+
+
+def check_index_list(gpu_list: np.ndarray, ref_list: np.ndarray, ref_scores: np.ndarray, n_valid, k: int,
+                     window: int):
+    """Decode-step index list [B, k + window]: the window part must match exactly; the live
+    entries must be distinct, the top-k part must avoid the window, and the live set may differ
+    from the oracle's only by slots whose oracle scores lie in the tie band of the k-th largest."""
+    assert gpu_list.shape == ref_list.shape
+    assert np.array_equal(gpu_list[:, k:], ref_list[:, k:]), "window part differs"
+    for b in range(gpu_list.shape[0]):
+        nv = int(n_valid[b])
+        wstart = nv - window
+        top = gpu_list[b, :k]
+        assert np.all((top < 0) | ((top >= 0) & (top < wstart))), "row %d: top-k entry inside the window" % b
+        live = gpu_list[b][gpu_list[b] >= 0]
+        assert len(np.unique(live)) == len(live), "row %d: duplicate index" % b
+        G, R = set(live.tolist()), set(ref_list[b][ref_list[b] >= 0].tolist())
+        if G != R:
+            o = ref_scores[b, :nv].astype(np.float64)
+            vk = np.sort(o)[::-1][min(k, nv) - 1]
+            tau = SCORE_RTOL * max(abs(vk), float(np.sqrt(np.mean(o * o))))
+            assert all(o[s] >= vk - tau for s in G - R), "row %d: extra slot outside the tie band" % b
+            assert all(o[s] <= vk + tau for s in R - G), "row %d: missing slot outside the tie band" % b
+            assert len(G) == len(R)

@@ -6,15 +6,13 @@ ragged rows, k around n_valid, masked / out-of-range / duplicate indices,
 sinks of either sign and no sink.  Full-size workloads are in
 test_gpu_fullsize.py.
 """
-import math
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synthetic
-from parity import (check_attn, check_scores, check_topk_own_scores, check_topk_same_scores, n_valid_rows)
+from parity import (check_attn, check_index_list, check_scores, check_topk_same_scores, n_valid_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -213,22 +211,7 @@ def _decode_case(dsa, w, label):
     ref_top = oracle.topk(ref_sc, w.index_topk, positions=w.positions, valid_len=w.valid_len)
     ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=w.positions,
                                valid_len=w.valid_len)
-    lst = step.index_list.cpu().numpy()
-    k = w.index_topk
-    assert np.array_equal(lst[:, k:], ref_list[:, k:]), "window part differs"
-    # top-k part: same set as the oracle's top-k up to the tie band, minus the window
-    for b in range(w.M):
-        wstart = int(nv[b]) - w.window
-        gtop = lst[b, :k]
-        assert np.all((gtop < 0) | (gtop < wstart))
-        G = set(lst[b][lst[b] >= 0].tolist())
-        R = set(ref_list[b][ref_list[b] >= 0].tolist())
-        assert len(G) == int((lst[b] >= 0).sum()), "duplicate in the GPU index list"
-        if G != R:  # allowed only inside the score tie band at the k-th boundary
-            o = ref_sc[b, : nv[b]].astype(np.float64)
-            vk = np.sort(o)[::-1][min(k, nv[b]) - 1]
-            tau = 1e-3 * max(abs(vk), float(np.sqrt(np.mean(o * o))))
-            assert all(o[s] >= vk - tau for s in G - R) and all(o[s] <= vk + tau for s in R - G)
+    check_index_list(step.index_list.cpu().numpy(), ref_list, ref_sc, nv, w.index_topk, w.window)
     ref_out, _ = oracle.sparse_attn(w.q, w.kv, w.sink, ref_list[:, None, :], sm_scale=w.sm_scale, dv=w.dv)
     err, rel = check_attn(step.out.float().cpu().numpy(), ref_out)
     return step, ref_sc, ref_list
