@@ -67,6 +67,7 @@ dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx
 
 struct decode_layout {
     size_t scores_off, scores_bytes;
+    size_t topk_off, topk_bytes;
     size_t list_off, list_bytes;
     size_t attn_off, attn_bytes;
     size_t total;
@@ -79,6 +80,9 @@ decode_layout layout_decode(const dsa_decode_args_t* a)
     L.scores_bytes = a->scores ? 0 : (size_t)a->B * a->S_max * sizeof(float);
     L.scores_off = off;
     off += round_up(L.scores_bytes);
+    L.topk_bytes = dsa::topk_workspace_bytes(a->B, a->S_max);
+    L.topk_off = off;
+    off += round_up(L.topk_bytes);
     const int32_t K_top = a->index_topk + a->window;
     L.list_bytes = a->index_list ? 0 : (size_t)a->B * K_top * sizeof(int32_t);
     L.list_off = off;
@@ -145,17 +149,16 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
     if (s != DSA_OK) return s;
     if (rows_per_seq == 1)
         return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
-                                                      valid_len, M, H, S_max, scale, scores, stream));
+                                                      valid_len, M, H, S_max, scale, scores, nullptr, 0, stream));
     return launch_status(dsa::launch_score_prefill(q, w, k_cache, positions, valid_len, M, rows_per_seq, H, S_max,
                                                    scale, (flags & DSA_SCORE_RELU) != 0, scores, stream));
 }
 
 size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk)
 {
-    (void)M;
-    (void)S_max;
     (void)index_topk;
-    return 0;
+    if (M < 1 || S_max < 1) return 0;
+    return dsa::topk_workspace_bytes(M, S_max);
 }
 
 dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions, int32_t valid_len,
@@ -164,10 +167,10 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
 {
     dsa_status_t s = check_topk(scores, M, S_max, index_topk, topk_idx);
     if (s != DSA_OK) return s;
-    if (workspace_bytes < dsa_topk_workspace_size(M, S_max, index_topk)) return DSA_ERR_WORKSPACE;
-    (void)workspace;
-    return launch_status(
-        dsa::launch_topk(scores, M, S_max, positions, valid_len, index_topk, 0, topk_idx, topk_scores, stream));
+    const size_t need = dsa::topk_workspace_bytes(M, S_max);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    return launch_status(dsa::launch_topk(scores, M, S_max, positions, valid_len, index_topk, 0, topk_idx,
+                                          topk_scores, workspace, false, stream));
 }
 
 size_t dsa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
@@ -208,14 +211,18 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
     float* scores = args->scores ? args->scores : reinterpret_cast<float*>(ws + L.scores_off);
     int32_t* list = args->index_list ? args->index_list : reinterpret_cast<int32_t*>(ws + L.list_off);
     void* attn_ws = L.attn_bytes ? static_cast<void*>(ws + L.attn_off) : nullptr;
+    void* topk_ws = L.topk_bytes ? static_cast<void*>(ws + L.topk_off) : nullptr;
     const int32_t K_top = args->index_topk + args->window;
 
+    // the scorer also clears the top-k workspace header, saving a launch
     hipError_t e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
                                             args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
-                                            args->B, args->H, args->S_max, args->index_scale, scores, stream);
+                                            args->B, args->H, args->S_max, args->index_scale, scores,
+                                            static_cast<uint32_t*>(topk_ws),
+                                            dsa::topk_header_words(args->B, args->S_max), stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
-                         args->window, list, nullptr, stream);
+                         args->window, list, nullptr, topk_ws, true, stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
                                 args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);

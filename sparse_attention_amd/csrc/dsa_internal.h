@@ -9,10 +9,13 @@
 
 namespace dsa {
 
-// Decode indexer score, one row per sequence (phi = identity).
+// Decode indexer score, one row per sequence (phi = identity).  If zero_words
+// > 0 the launch also clears zero_ptr[0 .. zero_words) (the top-k workspace
+// header of a fused decode step).
 hipError_t launch_score_decode(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
-                               int32_t H, int32_t S_max, float scale, float* scores, hipStream_t stream);
+                               int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
+                               size_t zero_words, hipStream_t stream);
 
 // Whether this build contains the prefill (per-head MFMA) scoring kernel.
 bool score_prefill_available();
@@ -25,9 +28,14 @@ hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cac
 // Top-k per row.  With window > 0 the output row has width k + window and
 // holds the top-k with in-window entries replaced by -1, followed by the
 // window positions (the decode-step index list).
+// Workspace bytes launch_topk needs for these shapes (0 for the row path),
+// and how many leading 32-bit words of it must be zero when it starts.
+size_t topk_workspace_bytes(int32_t M, int32_t S_max);
+size_t topk_header_words(int32_t M, int32_t S_max);
+// header_zeroed: the caller already cleared the header words in stream order.
 hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
                        int32_t valid_len, int32_t k, int32_t window, int32_t* out_idx, float* out_scores,
-                       hipStream_t stream);
+                       void* workspace, bool header_zeroed, hipStream_t stream);
 
 // Split count and partial-buffer size of the sparse attention launch.
 int sparse_attn_splits(int32_t B, int32_t S, int32_t Hq, int32_t K_top);

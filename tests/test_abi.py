@@ -84,7 +84,11 @@ def test_topk_validation(lib):
     assert f(_p(A), 0, 10, None, -1, 4, _p(A), None, None, 0, None) == ERR_SHAPE
     assert f(_p(A), 1, 10, None, -1, 0, _p(A), None, None, 0, None) == ERR_UNSUPPORTED
     assert f(_p(A), 1, 10, None, -1, 2049, _p(A), None, None, 0, None) == ERR_UNSUPPORTED
-    assert lib.dsa_topk_workspace_size(16, 32768, 1024) == 0
+    need = lib.dsa_topk_workspace_size(16, 32768, 1024)
+    assert need >= 16 * 32768 * 4
+    assert f(_p(A), 16, 32768, None, -1, 1024, _p(A), None, None, 0, None) == ERR_WORKSPACE
+    assert f(_p(A), 16, 32768, None, -1, 1024, _p(A), None, _p(A), need - 1, None) == ERR_WORKSPACE
+    assert lib.dsa_topk_workspace_size(8192, 8192, 2048) == 0  # many short rows: one workgroup per row
 
 
 def test_sparse_attn_validation_and_workspace(lib):

@@ -112,11 +112,26 @@ def test_topk_edges(dsa, S_max, k):
         assert np.all(np.isneginf(tsc[i][~ok]))
 
 
-def test_topk_all_equal_row(dsa):
-    sc = np.zeros((2, 4000), np.float32)
-    announce("dsa_topk all-equal rows")
-    idx = dsa.dsa_topk(torch.from_numpy(sc).cuda(), 1000, valid_len=3999).cpu().numpy()
-    check_topk_same_scores(idx, sc, np.array([3999, 3999]), 1000)
+@pytest.mark.parametrize("S_max", [4000, 20000])
+def test_topk_all_equal_row(dsa, S_max):
+    """Every score ties: any k of them is a valid answer (row and chunked paths)."""
+    sc = np.zeros((2, S_max), np.float32)
+    announce("dsa_topk all-equal rows S_max=%d" % S_max)
+    idx = dsa.dsa_topk(torch.from_numpy(sc).cuda(), 1000, valid_len=S_max - 1).cpu().numpy()
+    check_topk_same_scores(idx, sc, np.array([S_max - 1, S_max - 1]), 1000)
+
+
+def test_topk_repeated_calls_reuse_workspace(dsa):
+    """The chunked path clears its workspace itself: back-to-back calls agree."""
+    g = np.random.default_rng(5)
+    sc = torch.from_numpy(g.standard_normal((5, 50000)).astype(np.float32)).cuda()
+    announce("dsa_topk repeated calls")
+    a = dsa.dsa_topk(sc, 1024)
+    b = dsa.dsa_topk(sc, 1024)
+    torch.cuda.synchronize()
+    for i in range(5):
+        assert set(a[i].tolist()) == set(b[i].tolist())
+    check_topk_same_scores(a.cpu().numpy(), sc.cpu().numpy(), np.full(5, 50000), 1024)
 
 
 # ------------------------------------------------------------------ sparse attention
