@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_decode_step",
-                    choices=["full_decode_step", "tiny_decode", "batched_decode", "fp8_long_decode"])
+                    choices=["full_decode_step", "tiny_decode", "batched_decode", "fp8_long_decode", "prefill"])
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-sample", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -87,6 +87,8 @@ def main():
     dsa.load_library()
     dev = torch.device("cuda:0")
     t0 = time.time()
+    if args.workload == "prefill":
+        return bench_prefill(args, torch, dsa, synthetic, dev)
     w = synthetic.make_workload(args.workload)
     log("generated %s in %.1fs" % (args.workload, time.time() - t0))
     c = lambda t: None if t is None else t.contiguous().to(dev)  # noqa: E731
@@ -221,6 +223,40 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_prefill(args, torch, dsa, synthetic, dev):
+    """Prefill indexer: causal per-head MFMA scoring of 8192 queries x 8192 keys, then top-2048."""
+    w = synthetic.make_workload("prefill")
+    c = lambda t: None if t is None else t.contiguous().to(dev)  # noqa: E731
+    gq, gw, gk, gpos = c(w.index_q), c(w.index_w), c(w.k_cache), c(w.positions)
+    S, H, D = w.index_q.shape
+    scores = torch.empty((S, S), dtype=torch.float32, device=dev)
+
+    def run_score():
+        dsa.dsa_index_score(gq, gw, gk, scale=w.index_scale, positions=gpos, rows_per_seq=S, out=scores)
+
+    for _ in range(args.warmup):
+        run_score()
+    torch.cuda.synchronize()
+    ms = event_time_ms(torch, run_score, args.steps)
+    pairs = S * (S + 1) // 2
+    flops = 2.0 * H * D * pairs
+    ms_topk = event_time_ms(torch, lambda: dsa.dsa_topk(scores, w.index_topk, positions=gpos), args.steps)
+    tflops = flops / ms / 1e9
+    log("prefill score %.1f us: %.1f TFLOP/s (%.1f%% of bf16 MFMA peak); top-k %.1f us" % (
+        ms * 1e3, tflops, 100 * tflops / MFMA_BF16_PEAK_TFLOPS, ms_topk * 1e3))
+    rec = {"metric": METRIC, "value": pairs / ms * 1e3, "unit": "query-key pairs/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "prefill", "queries": S, "keys": S, "index_heads": H, "head_dim": D,
+                      "index_topk": w.index_topk, "parallelism": "single-gpu"},
+           "kernels": {"score_prefill": {"us": ms * 1e3, "flops": flops, "TFLOP/s": tflops},
+                       "topk": {"us": ms_topk * 1e3}},
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "score_prefill"},
+           "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
 

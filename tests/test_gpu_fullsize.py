@@ -1,0 +1,117 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+Where the oracle cannot redo the whole workload in seconds, it computes
+sampled rows / sequences one by one (always including the first and last
+rows and rows around tile boundaries) and the rest is checked through
+properties that hold at any size (finite scores, exact mask bound, valid
+top-k sets).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from parity import (check_attn, check_index_list, check_scores, check_topk_own_scores, n_valid_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print("\n[gpu case] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_amd as m
+
+    m.load_library()
+    assert torch.cuda.is_available(), "no GPU visible"
+    return m
+
+
+def _cuda(t):
+    return None if t is None else t.contiguous().cuda()
+
+
+def _decode_indexer(dsa, w, rows):
+    """Score + top-k of a decode indexer workload on the GPU; oracle on `rows`."""
+    pos = None if w.positions is None else w.positions.numpy()
+    nv = n_valid_rows(pos, w.valid_len, w.M, w.S_max)
+    scores = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                                 k_scale=_cuda(w.k_scale), positions=_cuda(w.positions), valid_len=w.valid_len)
+    idx = dsa.dsa_topk(scores, w.index_topk, positions=_cuda(w.positions), valid_len=w.valid_len)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    mb = np.float32(oracle.mask_bound())
+    assert np.isfinite(sc).all()
+    for r in range(w.M):  # properties on every row
+        assert np.all(sc[r, nv[r]:] == mb)
+    rows = np.asarray(rows)
+    sub_pos = None if w.positions is None else w.positions[rows]
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache[rows],
+                             k_scale=None if w.k_scale is None else w.k_scale[rows], scale=w.index_scale,
+                             positions=sub_pos, valid_len=w.valid_len)
+    check_scores(sc[rows], ref, nv[rows], oracle.mask_bound())
+    check_topk_own_scores(idx.cpu().numpy()[rows], ref, nv[rows], w.index_topk)
+
+
+def test_fullsize_batched_decode(dsa):
+    w = synthetic.make_workload("batched_decode")
+    announce("batched_decode full: 16 x 32768 slots, 64 heads, top-1024 (all rows)")
+    _decode_indexer(dsa, w, range(w.M))
+
+
+def test_fullsize_fp8_long_decode(dsa):
+    w = synthetic.make_workload("fp8_long_decode")
+    announce("fp8_long_decode full: 4 x 131072 fp8 slots, 64 heads, top-2048 (all rows)")
+    _decode_indexer(dsa, w, range(w.M))
+
+
+def test_fullsize_prefill(dsa):
+    w = synthetic.make_workload("prefill")
+    S = w.S_max
+    announce("prefill full: 8192 queries x 8192 keys causal, 64 heads, top-2048 (sampled rows)")
+    scores = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                                 positions=_cuda(w.positions), rows_per_seq=w.rows_per_seq)
+    idx = dsa.dsa_topk(scores, w.index_topk, positions=_cuda(w.positions))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 7, 8, 31, 32, 33, 1000, 2046, 2047, 2048, 4095, 4096, 6000, 8190, 8191])
+    sc = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
+    # all 8192 rows share one cache: the oracle rows map to it with rows_per_seq = len(rows)
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache, scale=w.index_scale,
+                             positions=w.positions[rows], rows_per_seq=len(rows))
+    check_scores(sc, ref, rows + 1, oracle.mask_bound())
+    check_topk_own_scores(idx.cpu().numpy()[rows], ref, rows + 1, w.index_topk)
+    full = scores.cpu().numpy()
+    assert np.isfinite(full).all()
+    tri = np.triu(np.ones((64, 64), bool), 1)  # spot-check the mask bound above the diagonal
+    assert np.all(full[:64, :64][tri] == np.float32(oracle.mask_bound()))
+
+
+def test_fullsize_decode_step(dsa):
+    w = synthetic.make_workload("full_decode_step")
+    announce("full_decode_step full: 64 x 65536 slots, top-1024 + window 128, 128 heads, 576/512 (sampled)")
+    step = dsa.dsa_decode_step(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), positions=_cuda(w.positions),
+                               valid_len=w.valid_len, index_scale=w.index_scale, index_topk=w.index_topk,
+                               window=w.window, q=_cuda(w.q), kv=_cuda(w.kv), attn_sink=_cuda(w.sink),
+                               sm_scale=w.sm_scale, dv=w.dv)
+    torch.cuda.synchronize()
+    rows = np.array([0, 17, 42, 63])
+    nv = n_valid_rows(w.positions.numpy(), w.valid_len, w.M, w.S_max)
+    ref_sc = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache[rows], scale=w.index_scale,
+                                positions=w.positions[rows])
+    check_scores(step.scores.cpu().numpy()[rows], ref_sc, nv[rows], oracle.mask_bound())
+    ref_top = oracle.topk(ref_sc, w.index_topk, positions=w.positions[rows])
+    ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=w.positions[rows])
+    check_index_list(step.index_list.cpu().numpy()[rows], ref_list, ref_sc, nv[rows], w.index_topk, w.window)
+    ref_out, _ = oracle.sparse_attn(w.q[rows], w.kv[rows], w.sink, ref_list[:, None, :], sm_scale=w.sm_scale,
+                                    dv=w.dv)
+    check_attn(step.out.float().cpu().numpy()[rows], ref_out)
+    out = step.out.float().cpu().numpy()
+    assert np.isfinite(out).all()
+    lst = step.index_list.cpu().numpy()
+    for b in range(w.M):  # every sequence: a valid, duplicate-free list with the exact window
+        live = lst[b][lst[b] >= 0]
+        assert len(np.unique(live)) == len(live) and live.max() < nv[b]
+        assert np.array_equal(lst[b, w.index_topk:], np.arange(nv[b] - w.window, nv[b]))

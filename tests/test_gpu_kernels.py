@@ -88,6 +88,37 @@ def test_score_decode_fp8_all_codes(dsa):
     _score_case(dsa, w, "fp8 all codes")
 
 
+@pytest.mark.parametrize("S,H,relu", [(300, 64, False), (300, 64, True), (77, 4, False), (130, 40, True),
+                                       (513, 64, False)])
+def test_score_prefill_causal(dsa, S, H, relu):
+    w = synthetic.make_workload("prefill", S=S, H=H, topk=64)
+    announce("dsa_index_score prefill S=%d H=%d relu=%s" % (S, H, relu))
+    got = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                              positions=_cuda(w.positions), rows_per_seq=w.rows_per_seq, relu=relu)
+    torch.cuda.synchronize()
+    ref = oracle.index_score(w.index_q, w.index_w, w.k_cache, scale=w.index_scale, positions=w.positions,
+                             rows_per_seq=w.rows_per_seq, relu=relu)
+    check_scores(got.cpu().numpy(), ref, np.arange(1, S + 1), oracle.mask_bound())
+
+
+def test_score_prefill_several_sequences_with_offset(dsa):
+    """3 sequences of 100 query rows each; each sequence's cache has 150 slots and its queries
+    start at position 20 (chunked prefill); plus a valid_len cap."""
+    g = np.random.default_rng(9)
+    n_seq, rps, S_max, H = 3, 100, 150, 64
+    q = torch.from_numpy(g.standard_normal((n_seq * rps, H, 128)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(g.standard_normal((n_seq * rps, H)).astype(np.float32))
+    k = torch.from_numpy(g.standard_normal((n_seq, S_max, 128)).astype(np.float32)).to(torch.bfloat16)
+    pos = torch.from_numpy(np.tile(np.arange(20, 20 + rps), n_seq).astype(np.int32))
+    for vl in (-1, 90):
+        announce("dsa_index_score prefill n_seq=3 rows_per_seq=100 valid_len=%d" % vl)
+        got = dsa.dsa_index_score(_cuda(q), _cuda(w), _cuda(k), scale=0.1, positions=_cuda(pos), valid_len=vl,
+                                  rows_per_seq=rps)
+        torch.cuda.synchronize()
+        ref = oracle.index_score(q, w, k, scale=0.1, positions=pos, valid_len=vl, rows_per_seq=rps)
+        check_scores(got.cpu().numpy(), ref, n_valid_rows(pos.numpy(), vl, n_seq * rps, S_max), oracle.mask_bound())
+
+
 # ------------------------------------------------------------------ top-k
 
 @pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (70000, 2048), (3000, 2048)])
