@@ -22,6 +22,18 @@ __device__ __forceinline__ int n_valid_of(const int32_t* positions, int32_t vali
     return (int)n;
 }
 
+// Same as n_valid_of in 32-bit arithmetic (cheaper when evaluated on the scalar unit).
+__device__ __forceinline__ int n_valid_of32(const int32_t* positions, int32_t valid_len, int32_t r, int32_t S_max)
+{
+    int n = S_max;
+    if (positions) {
+        const int p = positions[r];
+        n = p < S_max ? p + 1 : S_max;  // no overflow: p + 1 <= S_max
+    }
+    if (valid_len >= 0 && valid_len < n) n = valid_len;
+    return n < 0 ? 0 : n;
+}
+
 // The two bfloat16 halves of a 32-bit word as fp32 (low half = lower address).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }

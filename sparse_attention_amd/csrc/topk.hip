@@ -29,8 +29,9 @@
 //                   workgroups' writes visible; an in-kernel "last
 //                   workgroup" hand-off would need a device-scope fence,
 //                   which on these multi-XCD parts writes back the L2.
-//  * row path (many short rows, e.g. prefill): one 1024-thread workgroup per
-//    row runs all digits over the row with LDS histograms.
+//  * row path (many short rows, e.g. prefill): one workgroup per row runs
+//    all digits with LDS histograms; rows of up to 8192 slots are read once
+//    into LDS, longer rows are re-read from memory per digit.
 //
 // The decode step uses the same kernels to emit its index list: with
 // window > 0 a selected slot inside the window [n_valid - window, n_valid)
@@ -49,6 +50,8 @@ constexpr int kCoarse = 256;  // top 8 key bits: sign + 7 exponent bits
 constexpr int kCtrl = 4;      // per-row counters: above-count, candidate count, (2 spare)
 constexpr int kHeaderWords = kBins + kCoarse + kCtrl;  // per-row words zeroed before each call
 constexpr int kResolveCap = 8192;  // candidates resolved from LDS; more are re-read from HBM
+constexpr int kRowLdsThreads = 512;
+constexpr int kRowCap = 8192;      // row path: rows up to this many slots are held in LDS
 
 // ---------------------------------------------------------------- helpers
 
@@ -175,6 +178,124 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         if (pos >= 0) {
             orow[pos] = emit(s, wstart);
             if (osc) osc[pos] = v;
+        }
+    }
+}
+
+// Row path for rows of at most kRowCap slots (16-byte aligned): the row is
+// read once with 16-byte loads into LDS as order keys, building the first
+// digit's histogram on the way; later digits and the output pass run on LDS.
+// Outputs are compacted per wave (ballot + one LDS atomic per wave).
+__global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
+    const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
+    int32_t k, int32_t window, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
+{
+    constexpr int NT = kRowLdsThreads;
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kRowCap];
+    __shared__ int hist[kBins];
+    __shared__ int wave_tot[NT / 64];
+    __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq;
+
+    const int r = (int)(gridDim.x - 1 - blockIdx.x);  // long rows first
+    const int nv = n_valid_of(positions, valid_len, r, S_max);
+    const int width = k + window;
+    const int wstart = nv - window;
+    const float* __restrict__ row = scores + (size_t)r * S_max;
+    int32_t* __restrict__ orow = out_idx + (size_t)r * width;
+    float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+
+    for (int i = t; i < window; i += NT) {
+        const int p = wstart + i;
+        orow[k + i] = p < 0 ? -1 : p;
+    }
+    if (nv <= k) {
+        for (int j = t; j < k; j += NT) {
+            const int s = j < nv ? j : -1;
+            orow[j] = s < 0 ? -1 : emit(s, wstart);
+            if (osc) osc[j] = s >= 0 ? row[s] : -INFINITY;
+        }
+        return;
+    }
+
+    for (int i = t; i < kBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    const int nv4 = (nv + 3) & ~3;  // <= S_max (a multiple of 4)
+    for (int s = 4 * t; s < nv4; s += 4 * NT) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + s);
+        u32x4 kk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t key = f32_order_key(__uint_as_float(v[e]));
+            kk[e] = key;
+            if (s + e < nv) atomicAdd(&hist[key >> 20], 1);
+        }
+        *reinterpret_cast<u32x4*>(keys + s) = kk;
+    }
+    __syncthreads();
+
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = k;
+    const int shifts[3] = {20, 8, 0};
+    const int bits[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+        const int nb = 1 << bits[pass];
+        const int sh = shifts[pass];
+        if (pass > 0) {
+            for (int i = t; i < nb; i += NT) hist[i] = 0;
+            __syncthreads();
+            for (int s = t; s < nv; s += NT) {
+                const uint32_t key = keys[s];
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1);
+            }
+            __syncthreads();
+        }
+        find_bucket<NT>(hist, nb, remaining, wave_tot, &sh_digit, &sh_above);
+        const int d = sh_digit;
+        remaining -= sh_above;
+        prefix |= (uint32_t)d << sh;
+        pmask |= (uint32_t)(nb - 1) << sh;
+        const bool exact = hist[d] == remaining;
+        __syncthreads();
+        if (exact) break;
+    }
+
+    if (t == 0) {
+        cnt_gt = 0;
+        cnt_eq = 0;
+    }
+    __syncthreads();
+    const int n_gt = k - remaining;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
+    for (int s0 = 0; s0 < nv; s0 += NT) {
+        const int s = s0 + t;
+        uint32_t key = 0;
+        bool gt = false, eq = false;
+        if (s < nv) {
+            key = keys[s];
+            gt = (key & pmask) > prefix;
+            eq = (key & pmask) == prefix;
+        }
+        const uint64_t bg = __ballot(gt);
+        const uint64_t be = __ballot(eq);
+        int bgt = 0, beq = 0;
+        if (lane == 0) {
+            if (bg) bgt = atomicAdd(&cnt_gt, __popcll(bg));
+            if (be) beq = atomicAdd(&cnt_eq, __popcll(be));
+        }
+        bgt = __shfl(bgt, 0, 64);
+        beq = __shfl(beq, 0, 64);
+        int pos = -1;
+        if (gt) {
+            pos = bgt + __popcll(bg & lt);
+        } else if (eq) {
+            const int tk = beq + __popcll(be & lt);
+            if (tk < remaining) pos = n_gt + tk;
+        }
+        if (pos >= 0) {
+            orow[pos] = emit(s, wstart);
+            if (osc) osc[pos] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
         }
     }
 }
@@ -448,8 +569,12 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
                        void* workspace, bool header_zeroed, hipStream_t stream)
 {
     if (!use_chunked(M, S_max)) {
-        topk_row_kernel<<<M, kRowThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window, out_idx,
-                                                       out_scores);
+        if (S_max <= kRowCap && (S_max & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0)
+            topk_row_lds_kernel<<<M, kRowLdsThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
+                                                                  out_idx, out_scores);
+        else
+            topk_row_kernel<<<M, kRowThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window, out_idx,
+                                                           out_scores);
         return hipGetLastError();
     }
     uint32_t* ghist = static_cast<uint32_t*>(workspace);
