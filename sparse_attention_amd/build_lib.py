@@ -23,6 +23,11 @@ CPP_SOURCES = ["dsa_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device options.  The attention kernel keeps its 128-register
+# output accumulator in VGPRs (MFMA results written to VGPRs, read-only MFMA
+# operands free to live in AGPRs); otherwise the compiler copies the whole
+# accumulator between AGPRs and VGPRs on every block.
+EXTRA = {"sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
@@ -35,7 +40,7 @@ def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [_hipcc(), "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+        cmd = [_hipcc(), "-x", "hip", *DEVICE, *EXTRA.get(src, []), *COMMON, "-c", path, "-o", obj]
     else:
         cmd = [_hipcc(), *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -47,7 +47,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    // one v_cvt_pk_bf16_f32 on gfx950 (round to nearest even, as f32_to_bf16_bits)
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // DPP lane exchanges inside a row of 16 lanes.

@@ -6,6 +6,8 @@
 #include <cstdint>
 #include <cstring>
 
+#include <climits>
+
 #include "dsa.h"
 #include "dsa_internal.h"
 
@@ -61,6 +63,7 @@ dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx
     if (Dqk < 32 || Dqk > DSA_MAX_ATTN_DIM || Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (Dv < 16 || Dv > Dqk || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if ((long long)B * S > 65535) return DSA_ERR_SHAPE;
+    if ((long long)S_kv * Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's KV rows: 32-bit offsets
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DSA_ERR_ALIGN;
     return DSA_OK;
 }
@@ -109,6 +112,7 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     if (a->Hq < 1) return DSA_ERR_SHAPE;
     if (a->Dqk < 32 || a->Dqk > DSA_MAX_ATTN_DIM || a->Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
+    if ((long long)a->S_max * a->Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // KV rows: 32-bit offsets
     if (!aligned16(a->index_q) || !aligned16(a->index_w) || !aligned16(a->k_cache) || !aligned16(a->q) ||
         !aligned16(a->kv) || !aligned16(a->out))
         return DSA_ERR_ALIGN;
@@ -188,6 +192,7 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
     if (s != DSA_OK) return s;
     const size_t need = dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
     return launch_status(dsa::launch_sparse_attn(q, kv, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale,
                                                  out, lse, workspace, stream));
 }

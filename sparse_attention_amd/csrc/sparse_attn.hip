@@ -4,33 +4,40 @@
 // sparse_attention_torch; kwkr.cn article on DeepSeek-V4-Pro
 // inference/kernel.py, sparse-attention section): every query head attends
 // to the KV rows listed in its token's index list (-1 or out-of-range
-// entries masked); the listed rows are processed in 64-entry blocks with an
-// online softmax (running max and sum-exp, history rescaled by
-// exp(old max - new max)); the learnable sink adds exp(sink - max) to the
-// denominator once, at the end.
+// entries masked); the listed rows are processed in blocks with an online
+// softmax (running max and sum-exp, history rescaled by exp(old max - new
+// max)); the learnable sink adds exp(sink - max) to the denominator once,
+// at the end.
 //
 // gfx950 design:
-//   * workgroup = (query token, group of 32 heads), 4 waves; wave w owns
-//     16 heads (w & 1) and one half of every 64-entry block (w >> 1), with
-//     its own online-softmax state; the two halves are merged through LDS at
-//     the end, so no partial results go to HBM.  The grid is XCD-aware:
-//     workgroup ids are dealt to the 8 XCDs round-robin, and all head groups
-//     of a token get ids on the same XCD so its KV rows are fetched from HBM
-//     once and re-read from that XCD's L2.
-//   * gather: the 64 listed KV rows of a block are copied straight from HBM
-//     into LDS with 16-byte global_load_lds (no registers), double-buffered
-//     so block b+1 streams in while block b is computed.  Rows are padded to
-//     an odd number of 16-byte units so MFMA operand reads are bank-conflict
-//     free.  Masked entries load row 0 (finite data) and get weight 0.
+//   * workgroup = (query token, group of 64 heads, split of the index list),
+//     4 waves, wave w owns 16 heads.  Few tokens (decode) would leave most
+//     CUs idle with one workgroup per token and head group, so the list is
+//     split in nsplit parts and a combine kernel merges the partial results
+//     (row max, sum and normalised output per split, kept in the workspace);
+//     with enough tokens nsplit = 1 and the main kernel writes the output.
+//     The grid is XCD-aware: the head groups of a (token, split) get ids on
+//     the same XCD so its KV rows come from HBM once and again from L2.
+//   * gather: the 32 listed KV rows of a block are copied straight from HBM
+//     into LDS with 16-byte buffer loads (no registers), double-buffered so
+//     block b+1 streams in while block b is computed.  The copy walks the
+//     block's 16-byte units flat (a wave's 64 lanes may span two rows); rows
+//     are padded to 74 units (576 dims) so both MFMA operand read patterns
+//     are bank-conflict free; masked entries load row 0 (finite data,
+//     weight 0).
 //   * QK^T: v_mfma_f32_16x16x32_bf16 with M = 16 entries, N = 16 heads,
 //     K = 32 dims; A = KV row slices (ds_read_b128), B = q held in registers.
 //   * P.V: the S accumulator layout (lane = head, 4 consecutive entries per
-//     lane group) is the B operand P^T of a 32-entry K step directly; the A
-//     operand V^T comes from row-major LDS with ds_read_b64_tr_b16, which
+//     lane group) is the B operand P^T of the 32-entry K step directly; the
+//     A operand V^T comes from row-major LDS with ds_read_b64_tr_b16, which
 //     hands each lane one value column across 4 consecutive rows.
-//   * softmax state in log2 units (exp2), fp32; O^T[v][head] in registers.
-//   * the block's 64 list entries live in the lanes of every wave (lane =
-//     entry): DMA row addresses come from readlane, the mask from a ballot.
+//   * softmax state in log2 units (exp2), fp32; O^T[v][head] in registers;
+//     cross-lane maxima and sums use v_permlane16/32_swap (no LDS traffic).
+//   * the block's 32 list entries live in the lanes of every wave (lane % 32
+//     = entry): DMA row addresses come from a lane shuffle, the mask from a
+//     ballot.
+#include <algorithm>
+
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -44,10 +51,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr int kHeadsPerGroup = 32;
-constexpr int kBlock = 64;            // index-list entries per block
+constexpr int kHeadsPerGroup = 64;   // 4 waves x 16 heads
+constexpr int kBlock = 32;           // index-list entries per block
+constexpr int kTargetGroups = 256;   // workgroups wanted to fill the chip
+constexpr int kMaxSplits = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw (byte-addressed) access
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
 {
@@ -59,39 +69,79 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
 // has completed: vmcnt(0), expcnt / lgkmcnt unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// KSTEPS: Dqk / 32; VT: Dv / 16; ROWU: padded row length in 16-B units (odd).
+// max / sum over the 4 lane groups g (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float group_max(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1]));
+}
+__device__ __forceinline__ float group_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+}
+
+// Gather of one block of 32 rows of ROWU units by 4 waves of 64 lanes:
+// value = instructions of the busiest wave, full = leading iterations in
+// range for every wave, units = LDS buffer size (the last instruction of a
+// wave may run past the block into this padding).
+template <int ROWU>
+struct GatherIters {
+    static constexpr int total = kBlock * ROWU;
+    static constexpr int value = (total + kThreads - 1) / kThreads;
+    static constexpr int full = total >= kThreads ? (total - kThreads) / kThreads + 1 : 0;
+    static constexpr int units = (total + 63) / 64 * 64;
+};
+
+// KSTEPS: Dqk / 32; VT: Dv / 16; ROWU: padded row length in 16-B units,
+// ROWU % 16 == 10 (the smallest such length >= Dqk / 8).  With that stride
+// both operand read patterns are free of LDS bank conflicts on gfx950: the
+// 16-byte QK reads (16 rows x one unit) and the transposed 8-byte PV reads
+// (4 rows x 32 bytes); odd strides such as 73 conflict on both (measured
+// with SQ_LDS_BANK_CONFLICT).
 // EXACT: the shape is exactly (32 KSTEPS, 16 VT), so every loop has a fixed
 // trip count; otherwise they are upper bounds and loops are predicated.
+// With nsplit > 1 the results go to part_o / part_ml instead of out / lse.
 template <int KSTEPS, int VT, int ROWU, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
     const int32_t* __restrict__ idx, int32_t BS, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
-    int32_t K_top, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse)
+    int32_t K_top, float sm_scale, int32_t nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml)
 {
-    __shared__ __attribute__((aligned(16))) u32x4 kvbuf0[kBlock * ROWU];
-    __shared__ __attribute__((aligned(16))) u32x4 kvbuf1[kBlock * ROWU];
+    __shared__ __attribute__((aligned(16))) u32x4 kvbuf0[GatherIters<ROWU>::units];
+    __shared__ __attribute__((aligned(16))) u32x4 kvbuf1[GatherIters<ROWU>::units];
 
     const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
     const int id = blockIdx.x;
     const int slot = id / kXcds;
     const int hg = slot % HG;
-    const int tok = (slot / HG) * kXcds + id % kXcds;  // b * S + s
-    if (tok >= BS) return;  // uniform
+    const int unit = (slot / HG) * kXcds + id % kXcds;  // (token, split)
+    if (unit >= BS * nsplit) return;  // uniform
+    const int tok = unit / nsplit;
+    const int split = unit - tok * nsplit;
     const int b = tok / S;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int n = lane & 15;       // MFMA column: head within the wave
     const int g = lane >> 4;       // MFMA lane group
-    const int eh = wave >> 1;      // entry half of each block
-    const int head = hg * kHeadsPerGroup + (wave & 1) * 16 + n;
+    const int head = hg * kHeadsPerGroup + wave * 16 + n;
     const bool head_ok = head < Hq;
     const int ksteps = EXACT ? KSTEPS : Dqk / 32;
     const int vtiles = EXACT ? VT : Dv / 16;
     const int dunits = EXACT ? 4 * KSTEPS : Dqk / 8;  // 16-B units per KV row
-    const int rowu = EXACT ? ROWU : (dunits + 1) | 1;  // padded, odd
-    const int nblk = (K_top + kBlock - 1) / kBlock;
+    const int rowu = EXACT ? ROWU : dunits + ((10 - dunits) & 15);  // padded: rowu % 16 == 10
+    const int nblk_all = (K_top + kBlock - 1) / kBlock;
+    const int bps = (nblk_all + nsplit - 1) / nsplit;
+    const int blk0 = split * bps;
+    const int nblk = max(0, min(nblk_all, blk0 + bps) - blk0);
     const int32_t* __restrict__ ilist = idx + (size_t)tok * K_top;
     const uint16_t* __restrict__ kvb = kv + (size_t)b * S_kv * Dqk;
 
@@ -104,37 +154,63 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             qreg[t] = (head_ok && t < ksteps) ? *reinterpret_cast<const u32x4*>(qh + 32 * t) : u32x4{0, 0, 0, 0};
     }
 
-    // Every wave keeps the 64 index-list entries of a block in its lanes
-    // (lane = entry).  fetch_idx issues an unconditional in-bounds load;
+    // Every wave keeps the 32 index-list entries of a block in its lanes
+    // (lane % 32 = entry).  fetch_idx issues an unconditional in-bounds load;
     // check_idx turns the loaded value into a row or -1 once it is used.
+    const int el = lane & 31;
     auto fetch_idx = [&](int blk) -> int {
-        const int j = blk * kBlock + lane;
+        const int j = (blk0 + blk) * kBlock + el;
         return ilist[j < K_top ? j : K_top - 1];
     };
     auto check_idx = [&](int blk, int t) -> int {
-        const int j = blk * kBlock + lane;
-        return (j < K_top && t >= 0 && t < S_kv) ? t : -1;
+        const int j = (blk0 + blk) * kBlock + el;
+        return (blk < nblk && j < K_top && t >= 0 && t < S_kv) ? t : -1;
     };
-    // Issue the LDS DMA of a block's rows (row r's index in lane r of rows_idx)
-    // into dst.  Wave w copies rows 16w .. 16w + 15; per row, one instruction
-    // per 64 consecutive 16-B units (the row index is wave-uniform, read with
-    // readlane, so the address is a scalar base plus the lane's offset).
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // Issue the LDS DMA of a block's rows (entry e's row in lane e of rows_idx)
+    // into dst: the block's 32 x rowu units are walked flat, 64 consecutive
+    // units per wave instruction.  Iterations that are in range for every
+    // wave run without a branch; the last one is guarded per wave (its lanes
+    // past the block fill the buffer's padding).  With rows of at least 64
+    // units a wave instruction spans at most two rows, whose indices come
+    // from readlane; otherwise each lane shuffles its row index.
+    // The copies are buffer loads (MUBUF) into LDS over this sequence's KV
+    // rows, not global_load_lds: the compiler treats a pending FLAT LDS copy
+    // as an outstanding LDS access of unknown order and would then drain
+    // every LDS operand read completely instead of counting them.  The
+    // buffer's byte bound (S_kv * Dqk * 2, below 2 GiB) makes any stray
+    // offset read zeros.
+    const __amdgpu_buffer_rsrc_t kv_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)((long long)S_kv * Dqk * 2), kBufferWord3);
     auto gather = [&](int rows_idx, u32x4* dst) {
-        const char* gbase = reinterpret_cast<const char*>(kvb);
-        for (int rr = 0; rr < kBlock / 4; ++rr) {
-            const int row = wave_u * (kBlock / 4) + rr;
-            int r = __builtin_amdgcn_readlane(rows_idx, row);
-            r = r >= 0 ? r : 0;  // masked entry: row 0 (finite data, weight 0)
-            const char* src = gbase + (size_t)r * (2 * Dqk);
-            u32x4* d = dst + row * rowu;
-            for (int c0 = 0; c0 < rowu; c0 += 64) {
-                const int c = c0 + lane;
-                if (c < rowu) {
-                    const int cs = c < dunits ? c : dunits - 1;  // pad unit: any valid address
-                    __builtin_amdgcn_global_load_lds(src + 16 * cs, (lds_void*)(d + c0), 16, 0, 0);
-                }
+        const int total = kBlock * rowu;
+        auto one = [&](const int u0) {
+            const int u = u0 + lane;
+            const int row = u / rowu;
+            const int col = u - row * rowu;
+            int r;
+            if (EXACT && ROWU >= 64) {
+                const int row0 = u0 / rowu;  // wave-uniform
+                const int ra = __builtin_amdgcn_readlane(rows_idx, row0);
+                const int rb = __builtin_amdgcn_readlane(rows_idx, row0 + 1 < kBlock ? row0 + 1 : row0);
+                r = row > row0 ? rb : ra;
+            } else {
+                r = __shfl(rows_idx, row < kBlock ? row : 0, 64);
             }
+            r = r >= 0 ? r : 0;  // masked entry or padding: row 0 (finite data, weight 0)
+            const int cs = col < dunits ? col : dunits - 1;  // pad unit: any valid address
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, r * (2 * Dqk) + 16 * cs, 0,
+                                                     0, 0);
+        };
+        constexpr int kIt = GatherIters<ROWU>::value;
+        constexpr int kFull = GatherIters<ROWU>::full;
+        if (EXACT) {
+#pragma unroll
+            for (int i = 0; i < kFull; ++i) one(64 * wave_u + kThreads * i);
+#pragma unroll
+            for (int i = kFull; i < kIt; ++i)
+                if (64 * wave_u + kThreads * i < total) one(64 * wave_u + kThreads * i);
+        } else {
+            for (int u0 = 64 * wave_u; u0 < total; u0 += kThreads) one(u0);
         }
     };
 
@@ -148,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     // prologue: indices of block 0 (checked) and block 1 (in flight), rows of block 0
     int cur_idx = check_idx(0, fetch_idx(0));
     int pending = fetch_idx(nblk > 1 ? 1 : 0);
-    gather(cur_idx, kvbuf0);
+    if (nblk > 0) gather(cur_idx, kvbuf0);
 
     // One block: its rows are in kb (a compile-time choice of kvbuf0 / kvbuf1,
     // so the compiler can tell the DMA into the other buffer never aliases
@@ -163,9 +239,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         const uint64_t valid = __ballot(cur_idx >= 0);
         cur_idx = nxt_idx;
 
-        // ---- S = KV . q^T : tiles c = 0, 1 (entries 32 eh + 16 c + m); operands read one K step ahead
+        // ---- S = KV . q^T : tiles c = 0, 1 (entries 16 c + m); operands read one K step ahead
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const u32x4* ka0 = kb + (32 * eh + n) * rowu + g;
+        const u32x4* ka0 = kb + n * rowu + g;
         const u32x4* ka1 = ka0 + 16 * rowu;
         u32x4 a0 = ka0[0], a1 = ka1[0];
 #pragma unroll
@@ -183,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             }
         }
 
-        // ---- online softmax; lane (head n, group g) holds entries 32 eh + 16 c + 4 g + j.
+        // ---- online softmax; lane (head n, group g) holds entries 16 c + 4 g + j.
         // The reference max m_run only moves when a block exceeds it by more than
         // 8 (log2 units): p = 2^(s - m_run) then stays below 256, the result is
         // unchanged, and the accumulator rescale is skipped for the whole wave.
@@ -193,13 +269,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int e = 32 * eh + 16 * c + 4 * g + j;
+                const int e = 16 * c + 4 * g + j;
                 const float x = ((valid >> e) & 1) ? sacc[c][j] * qk_scale : -INFINITY;
                 sv[c][j] = x;
                 bmax = fmaxf(bmax, x);
             }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        bmax = group_max(bmax);
         const bool upd = bmax > m_run + 8.f;  // also true for the first finite block max
         if (__any(upd)) {
             // a real branch: without the asm statement the compiler if-converts
@@ -226,10 +301,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         const u32x4 pb = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                           pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
 
-        // ---- O^T += V^T . P^T over this wave's 32 entries (one K step)
+        // ---- O^T += V^T . P^T over the block's 32 entries (one K step)
         // transposed reads: lane i of group g addresses row R0 + i/4, value column v0 + 4 (i%4)
         const int i16 = lane & 15;
-        const int r0 = 32 * eh + 4 * g + (i16 >> 2);
+        const int r0 = 4 * g + (i16 >> 2);
         const char* vb0 = reinterpret_cast<const char*>(kb) + (size_t)r0 * rowu * 16 + 8 * (i16 & 3);
         const char* vb1 = vb0 + 16 * rowu * 16;
         auto vt_operand = [&](int v) -> u32x4 {
@@ -253,96 +328,185 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             }
         }
     };
+    // Scalar loads of the output pointers must not stay in flight across the
+    // block loop: a pending scalar load forces every LDS wait in the loop to
+    // drain completely (scalar loads may return out of order).
+    __asm__ volatile("" ::"s"(out), "s"(lse), "s"(part_o), "s"(part_ml), "s"(sink));
     for (int blk = 0; blk < nblk; blk += 2) {
         run_block(blk, kvbuf0, kvbuf1);
         if (blk + 1 < nblk) run_block(blk + 1, kvbuf1, kvbuf0);
     }
+    if (nblk == 0) wait_vmem();  // the index prefetch
 
-    // ---- merge the two entry halves through LDS (reusing the KV buffers)
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    __syncthreads();  // all waves done with the KV buffers
-    float* xch = reinterpret_cast<float*>(kvbuf0) + (wave & 1) * (VT * 4 + 2) * 64;
-    if (eh == 1) {
+    const float l_tot = group_sum(l_run);
+    if (!head_ok) return;
+    if (nsplit == 1) {
+        const float sk = sink ? sink[head] * kLog2e : -INFINITY;
+        float inv = 0.f, den = 0.f;
+        if (m_run != -INFINITY) {
+            den = l_tot + exp2f(sk - m_run);
+            inv = 1.f / den;
+        }
+        uint16_t* orow = out + ((size_t)tok * Hq + head) * Dv;
 #pragma unroll
-        for (int v = 0; v < VT; ++v)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xch[(v * 4 + j) * 64 + lane] = acc[v][j];
-        xch[VT * 4 * 64 + lane] = m_run;
-        xch[(VT * 4 + 1) * 64 + lane] = l_tot;
+        for (int v = 0; v < VT; ++v) {
+            if (v < vtiles) {
+                uint2 w;
+                w.x = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+                w.y = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
+                *reinterpret_cast<uint2*>(orow + 16 * v + 4 * g) = w;
+            }
+        }
+        if (lse && g == 0) {
+            float val;
+            if (m_run == -INFINITY) val = sink ? sink[head] : -INFINITY;
+            else val = (m_run + log2f(den)) / kLog2e;
+            lse[(size_t)tok * Hq + head] = val;
+        }
+        return;
     }
-    __syncthreads();
-    if (eh == 1 || !head_ok) return;
-    const float m_b = xch[VT * 4 * 64 + lane];
-    const float l_b = xch[(VT * 4 + 1) * 64 + lane];
-    const float M = fmaxf(m_run, m_b);
-    const float sk = sink ? sink[head] * kLog2e : -INFINITY;
-    float fa = 0.f, fb = 0.f, inv = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-        fa = exp2f(m_run - M);
-        fb = exp2f(m_b - M);
-        den = l_tot * fa + l_b * fb + exp2f(sk - M);
-        inv = 1.f / den;
-        fa *= inv;
-        fb *= inv;
-    }
-    uint16_t* orow = out + ((size_t)tok * Hq + head) * Dv;
+    // partial result of this split: normalised output, (max, sum) in log2 units
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const size_t ph = ((size_t)tok * nsplit + split) * Hq + head;
+    uint16_t* prow = part_o + ph * Dv;
 #pragma unroll
     for (int v = 0; v < VT; ++v) {
         if (v < vtiles) {
-            float o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = acc[v][j] * fa + xch[(v * 4 + j) * 64 + lane] * fb;
             uint2 w;
-            w.x = pack_bf16x2(o[0], o[1]);
-            w.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2*>(orow + 16 * v + 4 * g) = w;
+            w.x = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+            w.y = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
+            *reinterpret_cast<uint2*>(prow + 16 * v + 4 * g) = w;
         }
     }
-    if (lse && g == 0) {
+    if (g == 0) part_ml[ph] = make_float2(m_run, l_tot);
+}
+
+// Merge the nsplit partial results of every (token, head): one wave per
+// (token, head), each lane handles 8 consecutive output features.
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
+    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, const float* __restrict__ sink,
+    int32_t BS, int32_t Hq, int32_t Dv, int32_t nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
+{
+    const int wid = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (wid >= BS * Hq) return;  // uniform over the wave
+    const int lane = threadIdx.x & 63;
+    const int tok = wid / Hq;
+    const int head = wid - tok * Hq;
+    float wgt[kMaxSplits];
+    float M = sink ? sink[head] * kLog2e : -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < nsplit) M = fmaxf(M, part_ml[((size_t)tok * nsplit + s) * Hq + head].x);
+    float den = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        wgt[s] = 0.f;
+        if (s < nsplit) {
+            const float2 ml = part_ml[((size_t)tok * nsplit + s) * Hq + head];
+            if (ml.y > 0.f) wgt[s] = ml.y * exp2f(ml.x - M);
+            den += wgt[s];
+        }
+    }
+    const float sk = sink ? sink[head] * kLog2e : -INFINITY;
+    if (M != -INFINITY) den += exp2f(sk - M);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint16_t* orow = out + ((size_t)tok * Hq + head) * Dv;
+    for (int d = 8 * lane; d < Dv; d += 512) {
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < nsplit && wgt[s] > 0.f) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(part_o + (((size_t)tok * nsplit + s) * Hq + head) * Dv + d);
+                const float f = wgt[s] * inv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[2 * e] += f * bf16_lo(v[e]);
+                    o[2 * e + 1] += f * bf16_hi(v[e]);
+                }
+            }
+        }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+        *reinterpret_cast<u32x4*>(orow + d) = w;
+    }
+    if (lse && lane == 0) {
         float val;
-        if (M == -INFINITY) val = sink ? sink[head] : -INFINITY;
+        if (M == -INFINITY) val = -INFINITY;
+        else if (den <= 0.f) val = sink ? sink[head] : -INFINITY;
         else val = (M + log2f(den)) / kLog2e;
         lse[(size_t)tok * Hq + head] = val;
     }
 }
 
+int splits_for(int32_t BS, int32_t Hq, int32_t K_top)
+{
+    const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
+    const long long groups = (long long)BS * HG;
+    const int nblk = (K_top + kBlock - 1) / kBlock;
+    int ns = (int)((kTargetGroups + groups - 1) / groups);
+    ns = std::min(ns, kMaxSplits);
+    ns = std::min(ns, std::max(1, nblk / 4));  // at least 4 blocks per split
+    return std::max(ns, 1);
+}
+
 template <int KSTEPS, int VT, int ROWU, bool EXACT>
 hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink, const int32_t* idx, int32_t B,
                           int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale,
-                          void* out, float* lse, hipStream_t stream)
+                          void* out, float* lse, void* workspace, hipStream_t stream)
 {
     const int BS = B * S;
     const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
-    const int grid = (BS + kXcds - 1) / kXcds * kXcds * HG;
-    sparse_attn_kernel<KSTEPS, VT, ROWU, EXACT><<<grid, kThreads, 0, stream>>>(
+    const int ns = splits_for(BS, Hq, K_top);
+    uint16_t* part_o = nullptr;
+    float2* part_ml = nullptr;
+    if (ns > 1) {
+        part_o = static_cast<uint16_t*>(workspace);
+        const size_t o_bytes = ((size_t)BS * ns * Hq * Dv * sizeof(uint16_t) + 255) & ~(size_t)255;
+        part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
+    }
+    const long long units = (long long)BS * ns;
+    const long long grid = (units + kXcds - 1) / kXcds * kXcds * HG;
+    sparse_attn_kernel<KSTEPS, VT, ROWU, EXACT><<<(unsigned)grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), attn_sink, idx, BS, S, Hq, Dqk, Dv, S_kv,
-        K_top, sm_scale, static_cast<uint16_t*>(out), lse);
+        K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml);
+    if (ns > 1) {
+        const long long waves = (long long)BS * Hq;
+        sparse_attn_combine_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, stream>>>(
+            part_o, part_ml, attn_sink, BS, Hq, Dv, ns, static_cast<uint16_t*>(out), lse);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-int sparse_attn_splits(int32_t, int32_t, int32_t, int32_t) { return 1; }
+int sparse_attn_splits(int32_t B, int32_t S, int32_t Hq, int32_t K_top) { return splits_for(B * S, Hq, K_top); }
 
-size_t sparse_attn_partial_bytes(int32_t, int32_t, int32_t, int32_t, int32_t) { return 0; }
+size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
+{
+    const int ns = splits_for(B * S, Hq, K_top);
+    if (ns <= 1) return 0;
+    const size_t n = (size_t)B * S * ns * Hq;
+    const size_t o_bytes = (n * Dv * sizeof(uint16_t) + 255) & ~(size_t)255;
+    return o_bytes + n * sizeof(float2);
+}
 
 hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
-                              int32_t K_top, float sm_scale, void* out, float* lse, void*, hipStream_t stream)
+                              int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
+                              hipStream_t stream)
 {
     // Exact instances for the MLA decode shape (576 / 512) and the 192 / 128
     // shape; any other shape runs the predicated 576 / 512 instance.  ROWU
-    // covers (Dqk / 8 + 1) | 1 for every Dqk an instance accepts.
+    // covers Dqk / 8 + ((10 - Dqk / 8) & 15) for every Dqk an instance accepts.
     if (Dqk == 576 && Dv == 512)
-        return launch_variant<18, 32, 73, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                                lse, stream);
+        return launch_variant<18, 32, 74, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
+                                                lse, workspace, stream);
     if (Dqk == 192 && Dv == 128)
-        return launch_variant<6, 8, 25, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                              lse, stream);
-    return launch_variant<18, 32, 73, false>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                             lse, stream);
+        return launch_variant<6, 8, 26, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
+                                              lse, workspace, stream);
+    return launch_variant<18, 32, 74, false>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
+                                             lse, workspace, stream);
 }
 
 }  // namespace dsa
