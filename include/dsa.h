@@ -104,7 +104,7 @@ float dsa_mask_bound(void);
  *
  * Limits: D == 128; 1 <= H <= 128; M >= 1; S_max >= 1; M % rows_per_seq == 0.
  * rows_per_seq == 1 requires flags == 0 (DSA_ERR_UNSUPPORTED otherwise).
- * rows_per_seq > 1 requires bf16 keys and H <= 64.
+ * rows_per_seq > 1 requires bf16 keys, H <= 64 and S_max * 256 bytes below 2 GiB.
  */
 dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,
                              dsa_key_dtype_t k_dtype, const int32_t* positions, int32_t valid_len,

@@ -40,6 +40,7 @@ dsa_status_t check_index_score(const void* q, const float* w, const void* k_cach
     } else {
         if (k_dtype != DSA_KEY_BF16 || H > 64) return DSA_ERR_UNSUPPORTED;
         if (!dsa::score_prefill_available()) return DSA_ERR_UNSUPPORTED;
+        if ((long long)S_max * D * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's keys: 32-bit offsets
     }
     if (!aligned16(q) || !aligned16(k_cache)) return DSA_ERR_ALIGN;
     if (!aligned16(w) || !aligned16(scores) || (k_scale && !aligned16(k_scale))) return DSA_ERR_ALIGN;

@@ -19,7 +19,7 @@
 //     first copied to LDS with coalesced 16-byte DMA (loading the A layout
 //     straight from memory fetches every line 8 times);
 //   * the B operand comes from 128-key stages of K (32 KiB) copied HBM/L2 ->
-//     LDS with global_load_lds into two distinct, double-buffered LDS arrays,
+//     LDS with 16-byte buffer loads into two distinct, double-buffered arrays,
 //     one barrier per stage; 16-byte units are XOR-swizzled by key so operand
 //     reads are free of bank conflicts;
 //   * epilogue in registers: each lane holds 16 heads of one key per head
@@ -52,6 +52,7 @@ constexpr int kSubs = 4;                 // sub-tiles per stage
 constexpr int kStage = kSub * kSubs;     // keys per stage (one barrier each)
 constexpr int kStageU = kStage * 16;     // 16-byte units per stage
 constexpr int kLoads = kStageU / kThreads;
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw (byte-addressed) access
 constexpr int kRowQU = 64 * 16;         // 16-byte units of one query row (64 heads x 128 dims)
 static_assert(kLoads * kThreads == kStageU, "stage must split evenly over the workgroup");
 
@@ -104,22 +105,19 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(
     const int dk = tid >> 4;
     const int dch = (tid & 15) ^ (dk & 15);
     const uint32_t doff = (uint32_t)(dk * 256 + 16 * dch);  // bytes within the stage
+    // The copies are buffer loads (MUBUF) into LDS rather than
+    // global_load_lds: with a FLAT copy in flight the compiler drains every
+    // LDS operand read completely instead of counting them.  The buffer's
+    // byte bound (S_max * 256, below 2 GiB) returns zeros for keys past the
+    // cache, which are masked anyway.
+    const __amdgpu_buffer_rsrc_t k_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kseq, 0, S_max * 256, kBufferWord3);
     auto load_stage = [&](const int st, u32x4* dst) {
-        const int key0 = st * kStage;
-        if (key0 + kStage <= S_max) {
-            const char* src = kseq + (size_t)key0 * 256;
+        const uint32_t base = (uint32_t)(st * kStage) * 256u + doff;
 #pragma unroll
-            for (int i = 0; i < kLoads; ++i)
-                __builtin_amdgcn_global_load_lds(src + (doff + i * (kThreads / 16) * 256),
-                                                 (lds_void*)(dst + i * kThreads + 64 * wave), 16, 0, 0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kLoads; ++i) {
-                const int key = min(key0 + dk + (kThreads / 16) * i, S_max - 1);  // rows past the cache: any valid row
-                __builtin_amdgcn_global_load_lds(kseq + ((size_t)key * 256 + 16 * dch),
-                                                 (lds_void*)(dst + i * kThreads + 64 * wave), 16, 0, 0);
-            }
-        }
+        for (int i = 0; i < kLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(dst + i * kThreads + 64 * wave), 16,
+                                                     base + i * (kThreads / 16) * 256, 0, 0, 0);
     };
     // The wave's query row is staged through the key buffers (rows 0-1 in kt0,
     // rows 2-3 in kt1) before the key loop.  The copy is coalesced (each
@@ -129,13 +127,14 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(
     {
         const int hl = lane >> 4;                  // head within the instruction's 4
         const int cs = lane & 15;                  // slot within the head
-        const char* qrow = reinterpret_cast<const char*>(q + r * H * 128);
+        // heads past H read zeros (buffer bound: one row, H * 256 bytes)
+        const __amdgpu_buffer_rsrc_t q_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(q + r * H * 128), 0, H * 256, kBufferWord3);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int h = 4 * i + hl;
-            const int hc = h < H ? h : H - 1;      // heads past H: any valid head (zeroed below)
-            __builtin_amdgcn_global_load_lds(qrow + ((size_t)hc * 256 + 16 * (cs ^ (h & 15))),
-                                             (lds_void*)(qs + 64 * i), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(q_rsrc, (lds_void*)(qs + 64 * i), 16,
+                                                     (uint32_t)(h * 256 + 16 * (cs ^ (h & 15))), 0, 0, 0);
         }
     }
 
