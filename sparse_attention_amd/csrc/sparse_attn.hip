@@ -152,6 +152,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t)
             qreg[t] = (head_ok && t < ksteps) ? *reinterpret_cast<const u32x4*>(qh + 32 * t) : u32x4{0, 0, 0, 0};
+        // q only ever feeds MFMAs, which read AGPRs: keeping it there leaves the
+        // VGPRs to the accumulator and to operand reads in flight
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) __asm__("" : "+a"(qreg[t]));
     }
 
     // Every wave keeps the 32 index-list entries of a block in its lanes
@@ -239,23 +243,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         const uint64_t valid = __ballot(cur_idx >= 0);
         cur_idx = nxt_idx;
 
-        // ---- S = KV . q^T : tiles c = 0, 1 (entries 16 c + m); operands read one K step ahead
+        // ---- S = KV . q^T : tiles c = 0, 1 (entries 16 c + m); A operands read three K steps ahead
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         const u32x4* ka0 = kb + n * rowu + g;
         const u32x4* ka1 = ka0 + 16 * rowu;
-        u32x4 a0 = ka0[0], a1 = ka1[0];
+        u32x4 qa0[3], qa1[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            if (t < ksteps) {
+                qa0[t] = ka0[4 * t];
+                qa1[t] = ka1[4 * t];
+            }
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
             if (t < ksteps) {
-                u32x4 b0 = a0, b1 = a1;
-                if (t + 1 < ksteps) {
-                    b0 = ka0[4 * (t + 1)];
-                    b1 = ka1[4 * (t + 1)];
+                const u32x4 x0 = qa0[t % 3], x1 = qa1[t % 3];
+                if (t + 3 < ksteps) {
+                    qa0[t % 3] = ka0[4 * (t + 3)];
+                    qa1[t % 3] = ka1[4 * (t + 3)];
                 }
-                sacc[0] = mfma16(a0, qreg[t], sacc[0]);
-                sacc[1] = mfma16(a1, qreg[t], sacc[1]);
-                a0 = b0;
-                a1 = b1;
+                sacc[0] = mfma16(x0, qreg[t], sacc[0]);
+                sacc[1] = mfma16(x1, qreg[t], sacc[1]);
             }
         }
 
@@ -317,14 +325,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             a[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
             return a;
         };
-        u32x4 va = vt_operand(0);
+        u32x4 vring[3];  // V^T operands read three tiles ahead
+#pragma unroll
+        for (int v = 0; v < 3; ++v)
+            if (v < vtiles) vring[v] = vt_operand(v);
 #pragma unroll
         for (int v = 0; v < VT; ++v) {
             if (v < vtiles) {
-                u32x4 vn = va;
-                if (v + 1 < vtiles) vn = vt_operand(v + 1);
+                const u32x4 va = vring[v % 3];
+                if (v + 3 < vtiles) vring[v % 3] = vt_operand(v + 3);
                 acc[v] = mfma16(va, pb, acc[v]);
-                va = vn;
             }
         }
     };
