@@ -57,6 +57,17 @@ constexpr int kTargetGroups = 256;   // workgroups wanted to fill the chip
 constexpr int kMaxSplits = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+#ifndef DSA_QK_AHEAD
+#define DSA_QK_AHEAD 3
+#endif
+#ifndef DSA_PV_AHEAD
+#define DSA_PV_AHEAD 3
+#endif
+constexpr int kQkAhead = DSA_QK_AHEAD;  // K steps between a QK operand read and its MFMA
+constexpr int kPvAhead = DSA_PV_AHEAD;  // tiles between a V^T operand read and its MFMA
+constexpr int kSchedDsRead = 0x100;
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw (byte-addressed) access
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
@@ -116,14 +127,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     __shared__ __attribute__((aligned(16))) u32x4 kvbuf0[GatherIters<ROWU>::units];
     __shared__ __attribute__((aligned(16))) u32x4 kvbuf1[GatherIters<ROWU>::units];
 
+    // Workgroups are dealt to the XCDs round-robin (id % kXcds).  Each XCD
+    // takes whole tokens: all head groups and splits of a token share its
+    // L2, so the token's q and the gathered KV rows come from HBM once.
     const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
     const int id = blockIdx.x;
-    const int slot = id / kXcds;
-    const int hg = slot % HG;
-    const int unit = (slot / HG) * kXcds + id % kXcds;  // (token, split)
-    if (unit >= BS * nsplit) return;  // uniform
-    const int tok = unit / nsplit;
-    const int split = unit - tok * nsplit;
+    const int per_tok = HG * nsplit;
+    const int tok_per_xcd = (BS + kXcds - 1) / kXcds;
+    const int local = id / kXcds;
+    const int tok = (id % kXcds) * tok_per_xcd + local / per_tok;
+    if (local >= tok_per_xcd * per_tok || tok >= BS) return;  // uniform
+    const int rem = local % per_tok;
+    const int hg = rem % HG;
+    const int split = rem / HG;
     const int b = tok / S;
 
     const int tid = threadIdx.x;
@@ -187,34 +203,35 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)((long long)S_kv * Dqk * 2), kBufferWord3);
     auto gather = [&](int rows_idx, u32x4* dst) {
         const int total = kBlock * rowu;
-        auto one = [&](const int u0) {
+        // byte offset of each entry's row (lane e and lane e + 32 hold entry
+        // e); a masked entry or padding reads row 0 (finite data, weight 0)
+        const int eoff = max(rows_idx, 0) * (2 * Dqk);
+        // the row of unit u of the block; units past the last row are padding
+        auto row_of = [&](const int u) { const int row = u / rowu; return row < kBlock ? row : 0; };
+        auto one = [&](const int u0, const int roff) {
             const int u = u0 + lane;
-            const int row = u / rowu;
-            const int col = u - row * rowu;
-            int r;
-            if (EXACT && ROWU >= 64) {
-                const int row0 = u0 / rowu;  // wave-uniform
-                const int ra = __builtin_amdgcn_readlane(rows_idx, row0);
-                const int rb = __builtin_amdgcn_readlane(rows_idx, row0 + 1 < kBlock ? row0 + 1 : row0);
-                r = row > row0 ? rb : ra;
-            } else {
-                r = __shfl(rows_idx, row < kBlock ? row : 0, 64);
-            }
-            r = r >= 0 ? r : 0;  // masked entry or padding: row 0 (finite data, weight 0)
+            const int col = u - (u / rowu) * rowu;
             const int cs = col < dunits ? col : dunits - 1;  // pad unit: any valid address
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, r * (2 * Dqk) + 16 * cs, 0,
-                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff + 16 * cs, 0, 0, 0);
         };
         constexpr int kIt = GatherIters<ROWU>::value;
         constexpr int kFull = GatherIters<ROWU>::full;
         if (EXACT) {
+            // Every lane's row offsets for all of this wave's copy instructions,
+            // as independent cross-lane reads, then the loads: no chain of
+            // dependent scalar and vector steps in front of each load.
+            int roff[kIt];
 #pragma unroll
-            for (int i = 0; i < kFull; ++i) one(64 * wave_u + kThreads * i);
+            for (int i = 0; i < kIt; ++i)
+                roff[i] = __builtin_amdgcn_ds_bpermute(4 * row_of(64 * wave_u + kThreads * i + lane), eoff);
+#pragma unroll
+            for (int i = 0; i < kFull; ++i) one(64 * wave_u + kThreads * i, roff[i]);
 #pragma unroll
             for (int i = kFull; i < kIt; ++i)
-                if (64 * wave_u + kThreads * i < total) one(64 * wave_u + kThreads * i);
+                if (64 * wave_u + kThreads * i < total) one(64 * wave_u + kThreads * i, roff[i]);
         } else {
-            for (int u0 = 64 * wave_u; u0 < total; u0 += kThreads) one(u0);
+            for (int u0 = 64 * wave_u; u0 < total; u0 += kThreads)
+                one(u0, __builtin_amdgcn_ds_bpermute(4 * row_of(u0 + lane), eoff));
         }
     };
 
@@ -247,9 +264,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         const u32x4* ka0 = kb + n * rowu + g;
         const u32x4* ka1 = ka0 + 16 * rowu;
-        u32x4 qa0[3], qa1[3];
+        u32x4 qa0[kQkAhead], qa1[kQkAhead];
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
+        for (int t = 0; t < kQkAhead; ++t)
             if (t < ksteps) {
                 qa0[t] = ka0[4 * t];
                 qa1[t] = ka1[4 * t];
@@ -257,14 +274,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
             if (t < ksteps) {
-                const u32x4 x0 = qa0[t % 3], x1 = qa1[t % 3];
-                if (t + 3 < ksteps) {
-                    qa0[t % 3] = ka0[4 * (t + 3)];
-                    qa1[t % 3] = ka1[4 * (t + 3)];
+                const u32x4 x0 = qa0[t % kQkAhead], x1 = qa1[t % kQkAhead];
+                if (t + kQkAhead < ksteps) {
+                    qa0[t % kQkAhead] = ka0[4 * (t + kQkAhead)];
+                    qa1[t % kQkAhead] = ka1[4 * (t + kQkAhead)];
                 }
                 sacc[0] = mfma16(x0, qreg[t], sacc[0]);
                 sacc[1] = mfma16(x1, qreg[t], sacc[1]);
             }
+        }
+        if (EXACT) {  // keep the reads three K steps ahead of their MFMAs
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kQkAhead, 0);
+#pragma unroll
+            for (int t = 0; t < KSTEPS - kQkAhead; ++t) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kQkAhead, 0);
         }
 
         // ---- online softmax; lane (head n, group g) holds entries 16 c + 4 g + j.
@@ -272,16 +298,23 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         // 8 (log2 units): p = 2^(s - m_run) then stays below 256, the result is
         // unchanged, and the accumulator rescale is skipped for the whole wave.
         float sv[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[c][j] = sacc[c][j] * qk_scale;
+        if (valid != ~0ull) {  // masked entries (list padding, -1, out of range): logit -inf
+            const uint32_t bits = (uint32_t)(valid >> (4 * g));  // entry 16 c + 4 g + j at bit 16 c + j
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (!((bits >> (16 * c + j)) & 1u)) sv[c][j] = -INFINITY;
+        }
         float bmax = -INFINITY;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = 16 * c + 4 * g + j;
-                const float x = ((valid >> e) & 1) ? sacc[c][j] * qk_scale : -INFINITY;
-                sv[c][j] = x;
-                bmax = fmaxf(bmax, x);
-            }
+            for (int j = 0; j < 4; ++j) bmax = fmaxf(bmax, sv[c][j]);
         bmax = group_max(bmax);
         const bool upd = bmax > m_run + 8.f;  // also true for the first finite block max
         if (__any(upd)) {
@@ -289,12 +322,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             // this rarely taken rescale and runs it on every block
             __asm__ volatile("" ::: "memory");
             const float m_new = upd ? bmax : m_run;
-            const float alpha = upd ? exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+            const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
             l_run *= alpha;
 #pragma unroll
             for (int v = 0; v < VT; ++v) acc[v] *= alpha;
             m_run = m_new;
         }
+        // The hardware exp2 (v_exp_f32, about 1 ulp) is exact enough here: its
+        // argument is at most 8, and results below the fp32 normal range only
+        // come from entries that weigh less than 2^-126 of the block maximum.
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
         float p[2][4];
         float psum = 0.f;
@@ -302,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                p[c][j] = exp2f(sv[c][j] - msub);
+                p[c][j] = __builtin_amdgcn_exp2f(sv[c][j] - msub);
                 psum += p[c][j];
             }
         l_run += psum;
@@ -325,17 +361,26 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             a[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
             return a;
         };
-        u32x4 vring[3];  // V^T operands read three tiles ahead
+        u32x4 vring[kPvAhead];  // V^T operands read kPvAhead tiles ahead
 #pragma unroll
-        for (int v = 0; v < 3; ++v)
+        for (int v = 0; v < kPvAhead; ++v)
             if (v < vtiles) vring[v] = vt_operand(v);
 #pragma unroll
         for (int v = 0; v < VT; ++v) {
             if (v < vtiles) {
-                const u32x4 va = vring[v % 3];
-                if (v + 3 < vtiles) vring[v % 3] = vt_operand(v + 3);
+                const u32x4 va = vring[v % kPvAhead];
+                if (v + kPvAhead < vtiles) vring[v % kPvAhead] = vt_operand(v + kPvAhead);
                 acc[v] = mfma16(va, pb, acc[v]);
             }
+        }
+        if (EXACT) {  // V^T reads three tiles ahead of their MFMAs
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPvAhead, 0);
+#pragma unroll
+            for (int v = 0; v < VT - kPvAhead; ++v) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPvAhead, 0);
         }
     };
     // Scalar loads of the output pointers must not stay in flight across the
@@ -402,22 +447,35 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     const int lane = threadIdx.x & 63;
     const int tok = wid / Hq;
     const int head = wid - tok * Hq;
-    float wgt[kMaxSplits];
-    float M = sink ? sink[head] * kLog2e : -INFINITY;
+    // every load in flight at once: the (max, sum) pairs and this lane's
+    // first 8 output dims of every split (a split without entries holds
+    // zeros and gets weight 0)
+    float2 ml[kMaxSplits];
+    u32x4 v0[kMaxSplits];
+    const bool first = 8 * lane < Dv;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < nsplit) {
+            const size_t ph = ((size_t)tok * nsplit + s) * Hq + head;
+            ml[s] = part_ml[ph];
+            v0[s] = first ? *reinterpret_cast<const u32x4*>(part_o + ph * Dv + 8 * lane) : u32x4{0, 0, 0, 0};
+        }
+    }
+    const float sk = sink ? sink[head] * kLog2e : -INFINITY;
+    float M = sk;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s)
-        if (s < nsplit) M = fmaxf(M, part_ml[((size_t)tok * nsplit + s) * Hq + head].x);
+        if (s < nsplit) M = fmaxf(M, ml[s].x);
+    float wgt[kMaxSplits];
     float den = 0.f;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
         wgt[s] = 0.f;
         if (s < nsplit) {
-            const float2 ml = part_ml[((size_t)tok * nsplit + s) * Hq + head];
-            if (ml.y > 0.f) wgt[s] = ml.y * exp2f(ml.x - M);
+            if (ml[s].y > 0.f) wgt[s] = ml[s].y * exp2f(ml[s].x - M);
             den += wgt[s];
         }
     }
-    const float sk = sink ? sink[head] * kLog2e : -INFINITY;
     if (M != -INFINITY) den += exp2f(sk - M);
     const float inv = den > 0.f ? 1.f / den : 0.f;
     uint16_t* orow = out + ((size_t)tok * Hq + head) * Dv;
@@ -425,8 +483,9 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kMaxSplits; ++s) {
-            if (s < nsplit && wgt[s] > 0.f) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(part_o + (((size_t)tok * nsplit + s) * Hq + head) * Dv + d);
+            if (s < nsplit) {
+                const u32x4 v = d == 8 * lane ? v0[s] : *reinterpret_cast<const u32x4*>(
+                    part_o + (((size_t)tok * nsplit + s) * Hq + head) * Dv + d);
                 const float f = wgt[s] * inv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -475,8 +534,8 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
         const size_t o_bytes = ((size_t)BS * ns * Hq * Dv * sizeof(uint16_t) + 255) & ~(size_t)255;
         part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
     }
-    const long long units = (long long)BS * ns;
-    const long long grid = (units + kXcds - 1) / kXcds * kXcds * HG;
+    const long long tok_per_xcd = (BS + kXcds - 1) / kXcds;
+    const long long grid = tok_per_xcd * HG * ns * kXcds;
     sparse_attn_kernel<KSTEPS, VT, ROWU, EXACT><<<(unsigned)grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), attn_sink, idx, BS, S, Hq, Dqk, Dv, S_kv,
         K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml);
