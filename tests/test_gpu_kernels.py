@@ -121,7 +121,11 @@ def test_score_prefill_several_sequences_with_offset(dsa):
 
 # ------------------------------------------------------------------ top-k
 
-@pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (70000, 2048), (3000, 2048)])
+# paths: one workgroup per row with the row in LDS (S_max <= 8192, a
+# multiple of 4), rows cut into 4096-slot chunks (longer rows, fewer than
+# 1024), one workgroup per row re-reading the row otherwise
+@pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (65536, 2048), (40002, 512),
+                                     (70000, 2048), (3000, 2048)])
 def test_topk_edges(dsa, S_max, k):
     g = np.random.default_rng(S_max * 7 + k)
     nvs = sorted({0, 1, max(0, k - 1), k, k + 1, S_max // 2, S_max - 1, S_max})
@@ -152,17 +156,18 @@ def test_topk_all_equal_row(dsa, S_max):
     check_topk_same_scores(idx, sc, np.array([S_max - 1, S_max - 1]), 1000)
 
 
-def test_topk_repeated_calls_reuse_workspace(dsa):
-    """The chunked path clears its workspace itself: back-to-back calls agree."""
+@pytest.mark.parametrize("S_max", [50000, 70000])
+def test_topk_repeated_calls_reuse_workspace(dsa, S_max):
+    """Back-to-back calls agree (the chunked path clears its workspace itself)."""
     g = np.random.default_rng(5)
-    sc = torch.from_numpy(g.standard_normal((5, 50000)).astype(np.float32)).cuda()
-    announce("dsa_topk repeated calls")
+    sc = torch.from_numpy(g.standard_normal((5, S_max)).astype(np.float32)).cuda()
+    announce("dsa_topk repeated calls S_max=%d" % S_max)
     a = dsa.dsa_topk(sc, 1024)
     b = dsa.dsa_topk(sc, 1024)
     torch.cuda.synchronize()
     for i in range(5):
         assert set(a[i].tolist()) == set(b[i].tolist())
-    check_topk_same_scores(a.cpu().numpy(), sc.cpu().numpy(), np.full(5, 50000), 1024)
+    check_topk_same_scores(a.cpu().numpy(), sc.cpu().numpy(), np.full(5, S_max), 1024)
 
 
 # ------------------------------------------------------------------ sparse attention
