@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "DSA decode: indexer key-slots/s + sparse-attn tokens/s; % of HBM peak"
 PMC_FILE = os.path.join(ROOT, "profiles", "score_decode_full_decode_step.pmc.json")
-KERNEL_SOURCES = {"score_decode": "score_decode.hip", "topk": "topk.hip", "sparse_attn": "sparse_attn.hip"}
+KERNEL_SOURCES = {"score_decode": "score_decode.hip", "score_decode_relu": "score_decode_heads.hip", "topk": "topk.hip",
+                  "sparse_attn": "sparse_attn.hip"}
 
 
 def kernel_source_sha(name: str) -> str:
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--workload", default="full_decode_step",
                     choices=["full_decode_step", "tiny_decode", "batched_decode", "fp8_long_decode", "prefill"])
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--indexer-relu", action="store_true",
+                    help="indexer activation max(0, .) per head (per-head MFMA scorer) instead of the identity")
     ap.add_argument("--cpu-sample", type=int, default=64, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat oracle passes over the sample until this much time has been spent")
@@ -113,14 +116,14 @@ def main():
     if has_attn:
         step = dsa.DecodeStep(gq, gw, gk, k_scale=gks, positions=gpos, valid_len=w.valid_len,
                               index_scale=w.index_scale, index_topk=k, window=w.window, q=gaq, kv=gkv,
-                              attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv)
+                              attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv, relu=args.indexer_relu)
         run_step = step
     else:
         scores_buf = torch.empty((B, S_max), dtype=torch.float32, device=dev)
 
         def run_step():
             dsa.dsa_index_score(gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos,
-                                valid_len=w.valid_len, out=scores_buf)
+                                valid_len=w.valid_len, relu=args.indexer_relu, out=scores_buf)
             return dsa.dsa_topk(scores_buf, k, positions=gpos, valid_len=w.valid_len)
 
     for _ in range(args.warmup):
@@ -135,9 +138,10 @@ def main():
     scores_t = step.scores if has_attn else scores_buf
     kern = {}
     ms_score = event_time_ms(torch, lambda: dsa.dsa_index_score(
-        gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos, valid_len=w.valid_len, out=scores_t),
-        args.steps)
-    kern["score_decode"] = {"us": ms_score * 1e3, "bytes": score_bytes,
+        gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos, valid_len=w.valid_len,
+        relu=args.indexer_relu, out=scores_t), args.steps)
+    score_name = "score_decode_relu" if args.indexer_relu else "score_decode"
+    kern[score_name] = {"us": ms_score * 1e3, "bytes": score_bytes,
                             "GB/s": score_bytes / ms_score / 1e6,
                             "hbm_frac": score_bytes / ms_score / 1e6 / HBM_PEAK_GBS,
                             "key_slots_per_s": n_slots / ms_score * 1e3}
@@ -214,11 +218,12 @@ def main():
         "config": {"workload": args.workload, "batch": B, "cache_slots": S_max, "attendable_slots": n_slots,
                    "index_heads": H, "head_dim": D, "key_dtype": "fp8_e4m3" if w.key_fp8 else "bf16",
                    "index_topk": k, "window": w.window,
+                   "indexer_activation": "relu" if args.indexer_relu else "identity",
                    **({"attn_heads": int(w.q.shape[2]), "dqk": int(w.q.shape[3]), "dv": w.dv} if has_attn else {}),
                    "parallelism": "single-gpu"},
         "decode_tokens_per_s": B / ms_step * 1e3,
         "step_hbm_frac": step_bytes / ms_step / 1e6 / HBM_PEAK_GBS,
-        "indexer_key_slots_per_s": kern["score_decode"]["key_slots_per_s"],
+        "indexer_key_slots_per_s": kern[score_name]["key_slots_per_s"],
         "sparse_attn_tokens_per_s": kern["sparse_attn"]["tokens_per_s"] if has_attn else None,
         "kernels": kern,
         "roofline": roof,
@@ -285,7 +290,7 @@ def cpu_baseline(args, w, step, scores_t, nv, torch):
     sub_aq, sub_kv = (sub(w.q), sub(w.kv)) if step is not None else (None, None)
     def one_pass():
         sc = oracle.index_score(sub_q, sub_w, sub_k, k_scale=sub_ks, scale=w.index_scale,
-                                positions=pos, valid_len=w.valid_len, nthreads=threads)
+                                positions=pos, valid_len=w.valid_len, relu=args.indexer_relu, nthreads=threads)
         top = oracle.topk(sc, w.index_topk, positions=pos, valid_len=w.valid_len, nthreads=threads)
         lst = out = None
         if step is not None:
@@ -317,7 +322,12 @@ def cpu_baseline(args, w, step, scores_t, nv, torch):
         check_topk_own_scores(got, ref_sc, nv[rows], w.index_topk)
         parity["topk"] = "ok"
     if step is not None:
-        check_index_list(step.index_list.cpu().numpy()[rows], ref_list, ref_sc, nv[rows], w.index_topk, w.window)
+        gpu_list = step.index_list.cpu().numpy()[rows]
+        check_index_list(gpu_list, ref_list, ref_sc, nv[rows], w.index_topk, w.window)
+        if not np.array_equal(np.sort(gpu_list, axis=1), np.sort(ref_list, axis=1)):
+            # tied slots at the k-th score kept differently: attention parity on the step's own list
+            ref_out, _ = oracle.sparse_attn(sub_aq, sub_kv, w.sink, gpu_list[:, None, :], sm_scale=w.sm_scale,
+                                            dv=w.dv, nthreads=threads)
         err, rel = check_attn(step.out.float().cpu().numpy()[rows], ref_out)
         parity["index_list"] = "ok"
         parity["attention_max_abs_err"] = err

@@ -80,6 +80,8 @@ float dsa_mask_bound(void);
 /*
  * dsa_index_score -- lightning-indexer scores [NKI-V32] Returns and Notes;
  * [NKI-MX] :return: and Dimensions; [NEMO-DSV4] indexer_scores_torch.
+ * (The pages name no activation; the published DSA indexer applies ReLU per
+ * head, hence the flag.)
  *
  *   scores[r, s] = scale * sum_h w[r, h] * phi( sum_d q[r, h, d] * K[c, s, d] )
  *
@@ -103,8 +105,9 @@ float dsa_mask_bound(void);
  *   scores   [M, S_max] fp32 output, device
  *
  * Limits: D == 128; 1 <= H <= 128; M >= 1; S_max >= 1; M % rows_per_seq == 0.
- * rows_per_seq == 1 requires flags == 0 (DSA_ERR_UNSUPPORTED otherwise).
+ * rows_per_seq == 1: M <= 65535; with DSA_SCORE_RELU also H <= 64.
  * rows_per_seq > 1 requires bf16 keys, H <= 64 and S_max * 256 bytes below 2 GiB.
+ * Otherwise DSA_ERR_SHAPE / DSA_ERR_UNSUPPORTED.
  */
 dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,
                              dsa_key_dtype_t k_dtype, const int32_t* positions, int32_t valid_len,
@@ -179,7 +182,9 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
  * [NEMO-DSV4] build_dsv4_sparse_topk_indices).  The key cache slot s and
  * the kv slot s are the same position, so S_kv == S_max.
  *
- * The struct is versioned by struct_size (set it to sizeof(dsa_decode_args_t)).
+ * The struct is versioned by struct_size (set it to sizeof(dsa_decode_args_t));
+ * a struct_size that ends before index_flags is accepted, and the flags are
+ * then 0.
  */
 typedef struct dsa_decode_args {
     size_t struct_size;
@@ -206,6 +211,8 @@ typedef struct dsa_decode_args {
     float* lse;                 /* [B, 1, Hq] fp32 or NULL */
     float* scores;              /* [B, S_max] fp32 or NULL (then kept in workspace) */
     int32_t* index_list;        /* [B, index_topk + window] int32 or NULL (then workspace) */
+    /* added later; a struct_size that ends before this field reads as 0 */
+    uint32_t index_flags;       /* flags of dsa_index_score (DSA_SCORE_RELU: H <= 64) */
 } dsa_decode_args_t;
 
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args);

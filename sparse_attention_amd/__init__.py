@@ -44,7 +44,7 @@ class _DecodeArgs(ctypes.Structure):
         ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("attn_sink", ctypes.c_void_p),
         ("Hq", ctypes.c_int32), ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("scores", ctypes.c_void_p),
-        ("index_list", ctypes.c_void_p),
+        ("index_list", ctypes.c_void_p), ("index_flags", ctypes.c_uint32),
     ]
 
 
@@ -196,7 +196,7 @@ class DecodeStep:
 
     def __init__(self, index_q, index_w, k_cache, *, positions=None, valid_len: int = -1, index_scale: float,
                  index_topk: int, window: int, q, kv, attn_sink, sm_scale: float, dv: int, k_scale=None,
-                 keep_scores: bool = True, keep_index_list: bool = True):
+                 keep_scores: bool = True, keep_index_list: bool = True, relu: bool = False):
         _dev(index_q, "index_q", (torch.bfloat16,))
         _dev(index_w, "index_w", (torch.float32,))
         _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -233,6 +233,7 @@ class DecodeStep:
         a.out, a.lse = self.out.data_ptr(), self.lse.data_ptr()
         a.scores = None if self.scores is None else self.scores.data_ptr()
         a.index_list = None if self.index_list is None else self.index_list.data_ptr()
+        a.index_flags = DSA_SCORE_RELU if relu else 0
         self._args = a
         lib = load_library()
         self._nws = lib.dsa_decode_step_workspace_size(ctypes.byref(a))

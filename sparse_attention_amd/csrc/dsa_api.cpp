@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include <climits>
+#include <cstddef>
 
 #include "dsa.h"
 #include "dsa_internal.h"
@@ -35,7 +36,7 @@ dsa_status_t check_index_score(const void* q, const float* w, const void* k_cach
     if (H > 128) return DSA_ERR_UNSUPPORTED;
     if (flags & ~DSA_SCORE_RELU) return DSA_ERR_UNSUPPORTED;
     if (rows_per_seq == 1) {
-        if (flags != 0) return DSA_ERR_UNSUPPORTED;  // decode scoring folds heads: identity only
+        if ((flags & DSA_SCORE_RELU) && H > 64) return DSA_ERR_UNSUPPORTED;  // per-head MFMA path: 4 head tiles
         if (M > 65535) return DSA_ERR_SHAPE;
     } else {
         if (k_dtype != DSA_KEY_BF16 || H > 64) return DSA_ERR_UNSUPPORTED;
@@ -98,10 +99,19 @@ decode_layout layout_decode(const dsa_decode_args_t* a)
     return L;
 }
 
+// index_flags, or 0 for a struct that ends before the field
+uint32_t decode_flags(const dsa_decode_args_t* a)
+{
+    return a->struct_size >= offsetof(dsa_decode_args_t, index_flags) + sizeof(uint32_t) ? a->index_flags : 0u;
+}
+
 dsa_status_t check_decode(const dsa_decode_args_t* a)
 {
     if (!a) return DSA_ERR_NULL;
-    if (a->struct_size < sizeof(dsa_decode_args_t)) return DSA_ERR_UNSUPPORTED;
+    if (a->struct_size < offsetof(dsa_decode_args_t, index_flags)) return DSA_ERR_UNSUPPORTED;
+    const uint32_t flags = decode_flags(a);
+    if (flags & ~DSA_SCORE_RELU) return DSA_ERR_UNSUPPORTED;
+    if ((flags & DSA_SCORE_RELU) && a->H > 64) return DSA_ERR_UNSUPPORTED;
     if (!a->index_q || !a->index_w || !a->k_cache || !a->q || !a->kv || !a->out) return DSA_ERR_NULL;
     if (a->k_dtype != DSA_KEY_BF16 && a->k_dtype != DSA_KEY_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
     if (a->k_dtype == DSA_KEY_FP8_E4M3 && !a->k_scale) return DSA_ERR_NULL;
@@ -152,6 +162,9 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
 {
     dsa_status_t s = check_index_score(q, w, k_cache, k_scale, k_dtype, M, rows_per_seq, H, D, S_max, flags, scores);
     if (s != DSA_OK) return s;
+    if (rows_per_seq == 1 && (flags & DSA_SCORE_RELU))
+        return launch_status(dsa::launch_score_decode_heads(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3,
+                                                            positions, valid_len, M, H, S_max, scale, scores, stream));
     if (rows_per_seq == 1)
         return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
                                                       valid_len, M, H, S_max, scale, scores, nullptr, 0, stream));
@@ -220,15 +233,21 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
     void* topk_ws = L.topk_bytes ? static_cast<void*>(ws + L.topk_off) : nullptr;
     const int32_t K_top = args->index_topk + args->window;
 
-    // the scorer also clears the top-k workspace header, saving a launch
-    hipError_t e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
-                                            args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
-                                            args->B, args->H, args->S_max, args->index_scale, scores,
-                                            static_cast<uint32_t*>(topk_ws),
-                                            dsa::topk_header_words(args->B, args->S_max), stream);
+    const bool relu = (decode_flags(args) & DSA_SCORE_RELU) != 0;
+    hipError_t e;
+    if (relu) {  // per-head scorer; the top-k clears its own workspace header
+        e = dsa::launch_score_decode_heads(args->index_q, args->index_w, args->k_cache, args->k_scale,
+                                           args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
+                                           args->B, args->H, args->S_max, args->index_scale, scores, stream);
+    } else {  // the folded scorer also clears the top-k workspace header, saving a launch
+        e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
+                                     args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len, args->B,
+                                     args->H, args->S_max, args->index_scale, scores, static_cast<uint32_t*>(topk_ws),
+                                     dsa::topk_header_words(args->B, args->S_max), stream);
+    }
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
-                         args->window, list, nullptr, topk_ws, true, stream);
+                         args->window, list, nullptr, topk_ws, !relu, stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
                                 args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);

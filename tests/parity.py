@@ -51,7 +51,7 @@ def check_scores(gpu: np.ndarray, ref: np.ndarray, n_valid, mask_bound: float, r
         bad = err > tol
         assert not bad.any(), "row %d: %d scores out of tolerance, worst slot %d gpu %r oracle %r" % (
             i, bad.sum(), int(np.argmax(err - tol)), g[np.argmax(err - tol)], o[np.argmax(err - tol)])
-        worst = max(worst, float((err / np.maximum(np.abs(o), rms)).max()))
+        worst = max(worst, float((err / np.maximum(np.maximum(np.abs(o), rms), 1e-30)).max()))
     return worst
 
 

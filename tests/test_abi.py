@@ -72,7 +72,7 @@ def test_index_score_validation(lib):
     assert call(H=0) == ERR_SHAPE
     assert call(H=129) == ERR_UNSUPPORTED
     assert call(M=3, rps=2) == ERR_SHAPE
-    assert call(flags=1) == ERR_UNSUPPORTED       # relu on the folded decode path
+    assert call(flags=1, H=65) == ERR_UNSUPPORTED  # relu decode: per-head path, at most 64 heads
     assert call(flags=4) == ERR_UNSUPPORTED
     assert call(q=_p(A + 8)) == ERR_ALIGN
     assert call(kd=7) == ERR_UNSUPPORTED
@@ -140,5 +140,18 @@ def test_decode_step_validation(lib):
     a.q = None
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_NULL
     a.q = A
+    a.index_flags = 1
+    a.H = 65
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED  # relu: at most 64 heads
+    a.H = 64
+    a.index_flags = 2
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED  # unknown flag
+    a.index_flags = 0
     a.struct_size = 8
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED
+    # a struct without index_flags (the field is the last one) is still accepted: flags read as 0
+    old = ctypes.sizeof(m._DecodeArgs) - 8  # 4-byte field plus tail padding
+    assert old == m._DecodeArgs.index_flags.offset
+    a.struct_size = old
+    a.window = -1
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE  # validation went on past the size

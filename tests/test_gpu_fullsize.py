@@ -62,6 +62,24 @@ def test_fullsize_batched_decode(dsa):
     _decode_indexer(dsa, w, range(w.M))
 
 
+def test_fullsize_batched_decode_relu(dsa):
+    w = synthetic.make_workload("batched_decode")
+    announce("batched_decode full, ReLU indexer: 16 x 32768 slots, 64 heads (sampled rows)")
+    pos = w.positions.numpy()
+    nv = n_valid_rows(pos, w.valid_len, w.M, w.S_max)
+    scores = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                                 positions=_cuda(w.positions), relu=True)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    assert np.isfinite(sc).all()
+    for r in range(w.M):
+        assert np.all(sc[r, nv[r]:] == np.float32(oracle.mask_bound()))
+    rows = np.array([0, 5, 15])
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache[rows], scale=w.index_scale,
+                             positions=w.positions[rows], relu=True)
+    check_scores(sc[rows], ref, nv[rows], oracle.mask_bound())
+
+
 def test_fullsize_fp8_long_decode(dsa):
     w = synthetic.make_workload("fp8_long_decode")
     announce("fp8_long_decode full: 4 x 131072 fp8 slots, 64 heads, top-2048 (all rows)")
@@ -104,8 +122,10 @@ def test_fullsize_decode_step(dsa):
     check_scores(step.scores.cpu().numpy()[rows], ref_sc, nv[rows], oracle.mask_bound())
     ref_top = oracle.topk(ref_sc, w.index_topk, positions=w.positions[rows])
     ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=w.positions[rows])
-    check_index_list(step.index_list.cpu().numpy()[rows], ref_list, ref_sc, nv[rows], w.index_topk, w.window)
-    ref_out, _ = oracle.sparse_attn(w.q[rows], w.kv[rows], w.sink, ref_list[:, None, :], sm_scale=w.sm_scale,
+    gpu_list = step.index_list.cpu().numpy()[rows]
+    check_index_list(gpu_list, ref_list, ref_sc, nv[rows], w.index_topk, w.window)
+    # attention on the list the step built (validated above; tied slots may differ from the oracle's)
+    ref_out, _ = oracle.sparse_attn(w.q[rows], w.kv[rows], w.sink, gpu_list[:, None, :], sm_scale=w.sm_scale,
                                     dv=w.dv)
     check_attn(step.out.float().cpu().numpy()[rows], ref_out)
     out = step.out.float().cpu().numpy()

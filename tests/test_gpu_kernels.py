@@ -36,14 +36,15 @@ def _cuda(t):
 
 # ------------------------------------------------------------------ scores
 
-def _score_case(dsa, w, label):
-    announce("dsa_index_score %s M=%d S_max=%d H=%d fp8=%s" % (label, w.M, w.S_max, w.index_q.shape[1], w.key_fp8))
+def _score_case(dsa, w, label, relu=False):
+    announce("dsa_index_score %s M=%d S_max=%d H=%d fp8=%s relu=%s" % (label, w.M, w.S_max, w.index_q.shape[1],
+                                                                      w.key_fp8, relu))
     got = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
                               k_scale=_cuda(w.k_scale), positions=_cuda(w.positions), valid_len=w.valid_len,
-                              rows_per_seq=w.rows_per_seq)
+                              rows_per_seq=w.rows_per_seq, relu=relu)
     torch.cuda.synchronize()
     ref = oracle.index_score(w.index_q, w.index_w, w.k_cache, k_scale=w.k_scale, scale=w.index_scale,
-                             positions=w.positions, valid_len=w.valid_len, rows_per_seq=w.rows_per_seq)
+                             positions=w.positions, valid_len=w.valid_len, rows_per_seq=w.rows_per_seq, relu=relu)
     nv = n_valid_rows(None if w.positions is None else w.positions.numpy(), w.valid_len, w.M, w.S_max)
     return check_scores(got.cpu().numpy(), ref, nv, oracle.mask_bound())
 
@@ -71,6 +72,41 @@ def test_score_decode_valid_len_cap(dsa):
 def test_score_decode_fp8(dsa):
     w = synthetic.make_workload("fp8_long_decode", M=3, S_max=3000, vl_lo=1000, topk=64)
     _score_case(dsa, w, "fp8 scaled")
+
+
+# ReLU decode: per-head MFMA scorer (heads cannot be folded)
+@pytest.mark.parametrize("H", [1, 4, 16, 17, 64])
+def test_score_decode_relu_edges(dsa, H):
+    S_max = 5000  # a ragged last chunk and a ragged last 16-slot tile
+    w = synthetic.make_workload("batched_decode", M=9, H=H, S_max=S_max, pos_lo=0, topk=64)
+    w.positions = torch.tensor([-1, 0, 14, 15, 16, 511, 512, S_max - 2, S_max - 1], dtype=torch.int32)
+    _score_case(dsa, w, "relu edges H=%d" % H, relu=True)
+
+
+def test_score_decode_relu_multichunk(dsa):
+    # 40 rows x 40 chunks: the launch gives each workgroup a run of 4 chunks
+    # (2048 slots); valid lengths end on, beside and inside those runs, and
+    # the last chunk of every row is ragged
+    S_max = 20000
+    w = synthetic.make_workload("batched_decode", M=40, H=64, S_max=S_max, pos_lo=0, topk=64)
+    g = np.random.default_rng(11)
+    pos = g.integers(-1, S_max, size=40)
+    pos[:10] = [-1, 0, 2046, 2047, 2048, 4095, 6143, 8191, S_max - 33, S_max - 1]
+    w.positions = torch.from_numpy(pos.astype(np.int32))
+    _score_case(dsa, w, "relu multi-chunk runs", relu=True)
+    # fp8 keys, 16 rows x 79 chunks: runs of 3 chunks, the last run short
+    w = synthetic.make_workload("fp8_long_decode", M=16, S_max=40000, vl_lo=1000, topk=64)
+    _score_case(dsa, w, "relu fp8 multi-chunk runs", relu=True)
+
+
+def test_score_decode_relu_fp8(dsa):
+    w = synthetic.make_workload("fp8_long_decode", M=3, S_max=3000, vl_lo=1000, topk=64)
+    _score_case(dsa, w, "relu fp8 scaled", relu=True)
+    # negative and zero slot scales: the scale multiplies the dot before the activation
+    g = np.random.default_rng(3)
+    w.k_scale = torch.from_numpy((g.standard_normal((3, 3000)) * 0.01).astype(np.float32))
+    w.k_scale[:, ::7] = 0.0
+    _score_case(dsa, w, "relu fp8 signed scales", relu=True)
 
 
 def test_score_decode_fp8_all_codes(dsa):
@@ -246,24 +282,27 @@ def test_attn_peaked_softmax(dsa):
 
 # ------------------------------------------------------------------ decode step
 
-def _decode_case(dsa, w, label):
-    announce("dsa_decode_step %s B=%d S_max=%d topk=%d window=%d Hq=%d Dqk=%d" % (
-        label, w.M, w.S_max, w.index_topk, w.window, w.q.shape[2], w.q.shape[3]))
+def _decode_case(dsa, w, label, relu=False):
+    announce("dsa_decode_step %s B=%d S_max=%d topk=%d window=%d Hq=%d Dqk=%d relu=%s" % (
+        label, w.M, w.S_max, w.index_topk, w.window, w.q.shape[2], w.q.shape[3], relu))
     step = dsa.dsa_decode_step(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), k_scale=_cuda(w.k_scale),
                                positions=_cuda(w.positions), valid_len=w.valid_len, index_scale=w.index_scale,
                                index_topk=w.index_topk, window=w.window, q=_cuda(w.q), kv=_cuda(w.kv),
-                               attn_sink=_cuda(w.sink), sm_scale=w.sm_scale, dv=w.dv)
+                               attn_sink=_cuda(w.sink), sm_scale=w.sm_scale, dv=w.dv, relu=relu)
     torch.cuda.synchronize()
     pos = None if w.positions is None else w.positions.numpy()
     nv = n_valid_rows(pos, w.valid_len, w.M, w.S_max)
     ref_sc = oracle.index_score(w.index_q, w.index_w, w.k_cache, k_scale=w.k_scale, scale=w.index_scale,
-                                positions=w.positions, valid_len=w.valid_len)
+                                positions=w.positions, valid_len=w.valid_len, relu=relu)
     check_scores(step.scores.cpu().numpy(), ref_sc, nv, oracle.mask_bound())
     ref_top = oracle.topk(ref_sc, w.index_topk, positions=w.positions, valid_len=w.valid_len)
     ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, positions=w.positions,
                                valid_len=w.valid_len)
-    check_index_list(step.index_list.cpu().numpy(), ref_list, ref_sc, nv, w.index_topk, w.window)
-    ref_out, _ = oracle.sparse_attn(w.q, w.kv, w.sink, ref_list[:, None, :], sm_scale=w.sm_scale, dv=w.dv)
+    gpu_list = step.index_list.cpu().numpy()
+    check_index_list(gpu_list, ref_list, ref_sc, nv, w.index_topk, w.window)
+    # attention on the list the step built (validated just above): where scores tie at the k-th
+    # largest, the GPU may keep another tied slot than the oracle, and then attends to other rows
+    ref_out, _ = oracle.sparse_attn(w.q, w.kv, w.sink, gpu_list[:, None, :], sm_scale=w.sm_scale, dv=w.dv)
     err, rel = check_attn(step.out.float().cpu().numpy(), ref_out)
     return step, ref_sc, ref_list
 
@@ -276,6 +315,14 @@ def test_decode_step_mla_scaled(dsa):
     w = synthetic.make_workload("full_decode_step", B=3, S_max=3000, topk=256, window=128)
     w.positions = torch.tensor([2999, 100, 1500], dtype=torch.int32)
     _decode_case(dsa, w, "scaled full step")
+
+
+def test_decode_step_relu(dsa):
+    """ReLU indexer (per-head scorer) through the whole step; the top-k then clears its own workspace."""
+    _decode_case(dsa, synthetic.make_workload("tiny_decode"), "tiny_decode", relu=True)
+    w = synthetic.make_workload("full_decode_step", B=3, S_max=9000, topk=512, window=128)
+    w.positions = torch.tensor([8999, 100, 4500], dtype=torch.int32)
+    _decode_case(dsa, w, "scaled full step", relu=True)
 
 
 def test_decode_step_fp8_keys(dsa):
