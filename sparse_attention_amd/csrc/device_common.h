@@ -89,4 +89,14 @@ __device__ __forceinline__ uint32_t f32_order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Grid-stride clear of an unrelated buffer riding along with a 2-D launch
+// (saves the stream a launch of its own).
+__device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, size_t n)
+{
+    if (!n) return;
+    const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const size_t stride = (size_t)gridDim.x * gridDim.y * blockDim.x;
+    for (size_t i = wg * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 }  // namespace dsa

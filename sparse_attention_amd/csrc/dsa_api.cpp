@@ -164,7 +164,8 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
     if (s != DSA_OK) return s;
     if (rows_per_seq == 1 && (flags & DSA_SCORE_RELU))
         return launch_status(dsa::launch_score_decode_heads(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3,
-                                                            positions, valid_len, M, H, S_max, scale, scores, stream));
+                                                            positions, valid_len, M, H, S_max, scale, scores, nullptr, 0,
+                                                            stream));
     if (rows_per_seq == 1)
         return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
                                                       valid_len, M, H, S_max, scale, scores, nullptr, 0, stream));
@@ -235,11 +236,14 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
 
     const bool relu = (decode_flags(args) & DSA_SCORE_RELU) != 0;
     hipError_t e;
-    if (relu) {  // per-head scorer; the top-k clears its own workspace header
+    // either scorer also clears the top-k workspace header, saving a launch
+    if (relu) {
         e = dsa::launch_score_decode_heads(args->index_q, args->index_w, args->k_cache, args->k_scale,
                                            args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
-                                           args->B, args->H, args->S_max, args->index_scale, scores, stream);
-    } else {  // the folded scorer also clears the top-k workspace header, saving a launch
+                                           args->B, args->H, args->S_max, args->index_scale, scores,
+                                           static_cast<uint32_t*>(topk_ws),
+                                           dsa::topk_header_words(args->B, args->S_max), stream);
+    } else {
         e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
                                      args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len, args->B,
                                      args->H, args->S_max, args->index_scale, scores, static_cast<uint32_t*>(topk_ws),
@@ -247,7 +251,7 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
     }
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
-                         args->window, list, nullptr, topk_ws, !relu, stream);
+                         args->window, list, nullptr, topk_ws, true, stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
                                 args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);

@@ -21,7 +21,8 @@ hipError_t launch_score_decode(const void* q, const float* w, const void* k_cach
 // Decode indexer score with a per-head activation (max(0, .)): per-head MFMA, H <= 64.
 hipError_t launch_score_decode_heads(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                      bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
-                                     int32_t H, int32_t S_max, float scale, float* scores, hipStream_t stream);
+                                     int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
+                                     size_t zero_words, hipStream_t stream);
 
 bool score_prefill_available();
 

@@ -79,15 +79,6 @@ __device__ __forceinline__ void flush_stage(const float* stage, float* __restric
     }
 }
 
-// Grid-stride clear of an unrelated buffer riding along with this launch.
-__device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, size_t n)
-{
-    if (!n) return;
-    const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-    const size_t stride = (size_t)gridDim.x * gridDim.y * kThreads;
-    for (size_t i = wg * kThreads + threadIdx.x; i < n; i += stride) p[i] = 0u;
-}
-
 __device__ __forceinline__ float dot8_bf16(const float* qv, u32x4 v)
 {
     float p = qv[0] * bf16_lo(v.x);

@@ -33,7 +33,9 @@
 //     slot n; it applies max(0, .), weights by w[h] * scale, sums its heads,
 //     and the four lane groups are added with lane swaps;
 //   * scores are staged in LDS and written with 16-byte stores; chunks past
-//     n_valid only write the mask bound.
+//     n_valid only write the mask bound;
+//   * like the folded scorer, the launch can clear an unrelated buffer (the
+//     top-k workspace header of a decode step) on the side.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -82,8 +84,10 @@ template <bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ positions, int32_t valid_len, int32_t H,
-    int32_t S_max, int32_t cpw, float scale, float* __restrict__ scores)
+    int32_t S_max, int32_t cpw, float scale, float* __restrict__ scores, uint32_t* __restrict__ zero_ptr,
+    size_t zero_words)
 {
+    clear_words(zero_ptr, zero_words);
     __shared__ __attribute__((aligned(16))) float stage[kChunk * kMaxCpw];
     const int r = blockIdx.y;
     const int s0 = blockIdx.x * kChunk * cpw;
@@ -200,7 +204,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
 
 hipError_t launch_score_decode_heads(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                      bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
-                                     int32_t H, int32_t S_max, float scale, float* scores, hipStream_t stream)
+                                     int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
+                                     size_t zero_words, hipStream_t stream)
 {
     const int chunks = (S_max + kChunk - 1) / kChunk;
     const long long total = (long long)chunks * M;
@@ -209,11 +214,11 @@ hipError_t launch_score_decode_heads(const void* q, const float* w, const void* 
     if (key_fp8)
         score_decode_heads_kernel<true><<<grid, kThreads, 0, stream>>>(
             static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), k_scale, positions, valid_len,
-            H, S_max, cpw, scale, scores);
+            H, S_max, cpw, scale, scores, zero_ptr, zero_words);
     else
         score_decode_heads_kernel<false><<<grid, kThreads, 0, stream>>>(
             static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), nullptr, positions, valid_len,
-            H, S_max, cpw, scale, scores);
+            H, S_max, cpw, scale, scores, zero_ptr, zero_words);
     return hipGetLastError();
 }
 
