@@ -12,6 +12,9 @@ Functions follow the web pages cited in ``dsa_oracle.c``:
   * ``assemble``     -- top-k plus always-selected sliding window
   * ``sparse_attn``  -- two-pass softmax-with-sink attention over an index list
   * ``n_valid``      -- attendable slots of a row
+  * ``quantize_fp8_blocks`` / ``dequantize_fp8_blocks`` -- FP8 E4M3 block
+                        quantiser (binary32 decisions, nearest code, ties even)
+  * ``cache_write``  -- new keys stored at their positions, optionally quantised
 """
 from __future__ import annotations
 
@@ -57,6 +60,9 @@ def _load():
     lib.oracle_topk.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, ip]
     lib.oracle_assemble.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
     lib.oracle_sparse_attn.argtypes = [vp, ip, vp, ip, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, vp, vp, ip]
+    lib.oracle_encode_fp8_e4m3.argtypes = [vp, vp, i64]
+    lib.oracle_quantize_fp8_blocks.argtypes = [vp, i64, i32, ip, vp, vp]
+    lib.oracle_dequantize_fp8_blocks.argtypes = [vp, vp, i64, i32, vp]
     _lib = lib
     return lib
 
@@ -201,3 +207,99 @@ def sparse_attn(q, kv, sink, idx, *, sm_scale: float, dv: int, nthreads: int | N
     _load().oracle_sparse_attn(_ptr(qa), qt, _ptr(ka), kt, _ptr(sk), _ptr(ia), B, S, Hq, Dqk, dv, S_kv, K_top,
                                float(sm_scale), _ptr(out), _ptr(lse), nthreads or default_threads())
     return out, lse
+
+
+# ------------------------------------------------------------ key-cache write
+
+QUANT_BLOCK = 128  # elements per FP8 quantisation block ([V4-KERNEL] FP8 block quantisation)
+
+
+def _bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of a torch bfloat16 tensor or a uint16 array."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            assert x.dtype == torch.bfloat16
+            return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(x)
+    assert a.dtype == np.uint16
+    return a
+
+
+def encode_fp8_e4m3(y) -> np.ndarray:
+    """Nearest E4M3 codes (ties to even) of binary32 values with |y| <= 448."""
+    a = _np(y, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().oracle_encode_fp8_e4m3(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def quantize_fp8_blocks(x, *, round_scale: bool = False, block: int = QUANT_BLOCK):
+    """FP8 block quantisation of bfloat16 x [..., D] (D a multiple of block).
+
+    Returns (codes uint8 [..., D], scales float32 [..., D // block])."""
+    bits = _bf16_bits(x)
+    D = bits.shape[-1]
+    assert D % block == 0
+    n_blocks = bits.size // block
+    codes = np.empty(bits.shape, np.uint8)
+    scales = np.empty(bits.shape[:-1] + (D // block,), np.float32)
+    _load().oracle_quantize_fp8_blocks(_ptr(bits), n_blocks, block, int(bool(round_scale)), _ptr(codes),
+                                       _ptr(scales))
+    return codes, scales
+
+
+def dequantize_fp8_blocks(codes, scales, *, block: int = QUANT_BLOCK) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of value(code) * scale, rounded once."""
+    c = _np(codes, np.uint8)
+    sc = _np(scales, np.float32)
+    assert c.shape[-1] % block == 0 and sc.size * block == c.size
+    out = np.empty(c.shape, np.uint16)
+    _load().oracle_dequantize_fp8_blocks(_ptr(c), _ptr(sc), c.size // block, block, _ptr(out))
+    return out
+
+
+def cache_write(k_new, positions, k_cache, k_scale=None, *, rows_per_seq: int = 1, round_scale: bool = False,
+                qdq: bool = False):
+    """Key-cache write: token t of k_new [T, D] (bfloat16) goes to cache row
+    t // rows_per_seq at slot positions[t], in place at the token's position
+    ([NKI-V32] key_cache); tokens whose position is outside [0, S_max) are
+    not written.
+
+    * FP8 cache (``k_cache`` uint8 codes [n_seq, S_max, D] with ``k_scale``
+      float32 [n_seq, S_max, D // 128]): the key is block-quantised.
+    * bfloat16 cache (bit patterns uint16 or a bfloat16 tensor): the key is
+      stored as is, or with ``qdq`` quantised and dequantised back.
+
+    Returns updated copies (numpy): (codes, scales) or the bfloat16 bits."""
+    kb = _bf16_bits(k_new)
+    T, D = kb.shape
+    pos = _np(positions, np.int32)
+    assert pos.shape == (T,) and T % rows_per_seq == 0
+    fp8 = k_scale is not None
+    if fp8:
+        cache = np.array(_np(k_cache, np.uint8))
+        scales = np.array(_np(k_scale, np.float32))
+        codes, sc = quantize_fp8_blocks(kb, round_scale=round_scale)
+    else:
+        cache = np.array(_bf16_bits(k_cache))
+        if qdq:
+            codes, sc = quantize_fp8_blocks(kb, round_scale=round_scale)
+            vals = dequantize_fp8_blocks(codes, sc)
+        else:
+            vals = kb
+    n_seq, S_max, Dc = cache.shape
+    assert Dc == D and n_seq == T // rows_per_seq
+    for t in range(T):
+        c, p = t // rows_per_seq, int(pos[t])
+        if not 0 <= p < S_max:
+            continue
+        if fp8:
+            cache[c, p] = codes[t]
+            scales[c, p] = sc[t].reshape(scales[c, p].shape)
+        else:
+            cache[c, p] = vals[t]
+    return (cache, scales) if fp8 else cache

@@ -1,7 +1,8 @@
 /*
  * dsa_oracle.c -- plain, slow CPU oracle for the DeepSeek Sparse Attention
  * (DSA) hot path: lightning-indexer scores, top-k selection, window/top-k
- * index assembly and top-k sparse attention with an attention sink.
+ * index assembly, top-k sparse attention with an attention sink, and the
+ * key-cache write with FP8 block quantisation.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke entry point and
  * the CPU-baseline leg of the benchmark may call this code.  It shares no
@@ -32,6 +33,12 @@
  *     bfloat16 consumer never sees -inf [NKI-V32] Notes.
  *   - the sink is a logit in the units of the scaled scores, excluded from
  *     the max; with no sink the term is absent [V4-KERNEL] sparse attention.
+ *   - FP8 block quantisation: the pages fix no precision, yet its arithmetic
+ *     decides integer codes, so it is done in binary32 as a GPU kernel does
+ *     it: amax, scale = amax / 448, y = x / scale (each one IEEE binary32
+ *     operation), y clamped to [-448, 448], then the nearest E4M3 value with
+ *     ties to the even code.  An all-zero block gets scale 1.  The optional
+ *     power-of-two scale is the smallest power of two >= amax / 448.
  *
  * Inputs must be free of NaN.  Threads split independent rows (or
  * (batch, query, head) triples) statically; each output element is computed
@@ -96,6 +103,93 @@ void oracle_decode_fp8_e4m3(const uint8_t* src, double* dst, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
         dst[i] = fp8_e4m3_value(src[i]);
+}
+
+/* Nearest E4M3 code to y (finite, |y| <= 448), found by trying every
+ * non-negative finite code; of two equally near codes the even one (even
+ * mantissa) wins, i.e. round to nearest, ties to even.  The sign bit is y's,
+ * so a negative y that rounds to zero gives the code of -0. */
+static uint8_t fp8_e4m3_encode(float y)
+{
+    const double v = fabs((double)y);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        const double d = fabs(fp8_e4m3_value((uint8_t)c) - v);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+void oracle_encode_fp8_e4m3(const float* src, uint8_t* dst, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = fp8_e4m3_encode(src[i]);
+}
+
+/* bfloat16 nearest to a finite binary32 value, ties to even (the bfloat16
+ * keeps the upper 16 bits; the lower 16 decide the rounding). */
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* FP8 block quantiser, [V4-KERNEL] FP8 block quantisation (block of 128
+ * elements, scale = amax / 448 so the block fits E4M3's +-448; optional
+ * power-of-two scale).  x: n_blocks * block bfloat16 bit patterns; codes:
+ * same count; scales: one per block.  Every step is one binary32
+ * operation, see the file header. */
+void oracle_quantize_fp8_blocks(const uint16_t* x, int64_t n_blocks, int32_t block, int round_scale,
+                                uint8_t* codes, float* scales)
+{
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        const uint16_t* xb = x + b * block;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < block; ++i) {
+            const float a = fabsf((float)bf16_value(xb[i]));
+            if (a > amax)
+                amax = a;
+        }
+        float s = 1.0f;
+        if (amax > 0.0f) {
+            s = amax / 448.0f;
+            if (round_scale) {
+                int e;
+                const float m = frexpf(s, &e); /* s = m * 2^e, m in [0.5, 1) */
+                if (m != 0.5f)
+                    s = ldexpf(1.0f, e);
+            }
+        }
+        for (int32_t i = 0; i < block; ++i) {
+            float y = (float)bf16_value(xb[i]) / s;
+            if (y > 448.0f)
+                y = 448.0f;
+            if (y < -448.0f)
+                y = -448.0f;
+            codes[b * block + i] = fp8_e4m3_encode(y);
+        }
+        scales[b] = s;
+    }
+}
+
+/* Dequantised bfloat16 of the codes: value(code) * scale in binary32,
+ * rounded once to bfloat16 (the quantise-then-dequantise option of
+ * [V4-KERNEL] FP8 block quantisation). */
+void oracle_dequantize_fp8_blocks(const uint8_t* codes, const float* scales, int64_t n_blocks, int32_t block,
+                                  uint16_t* out)
+{
+    for (int64_t b = 0; b < n_blocks; ++b)
+        for (int32_t i = 0; i < block; ++i)
+            out[b * block + i] = bf16_round((float)fp8_e4m3_value(codes[b * block + i]) * scales[b]);
 }
 
 /* Element i of a tensor stored as dtype (F64 / BF16 / FP8 codes). */
