@@ -7,6 +7,8 @@
  *   dsa_sparse_attn   top-k sparse multi-query attention with attention sink
  *   dsa_decode_step   the three fused into one decode step on one stream,
  *                     with the always-selected sliding window
+ *   dsa_cache_write   new keys stored in the key cache at their positions,
+ *                     optionally FP8 block-quantised
  *
  * Sources (web pages, cited by title and section):
  *   [NKI-V32]   AWS Neuron "DeepSeek-V3.2 Sparse Indexer Kernel API Reference"
@@ -218,6 +220,45 @@ typedef struct dsa_decode_args {
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args);
 dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* flags of dsa_cache_write */
+#define DSA_CACHE_ROUND_SCALE 1u /* power-of-two scale: the smallest 2^e >= amax / 448 */
+#define DSA_CACHE_QDQ 2u         /* bf16 cache: store the key quantised and dequantised again */
+
+/*
+ * dsa_cache_write -- store each token's new indexer key in the key cache,
+ * in place at the token's position ([NKI-V32] key_cache), optionally
+ * quantised to FP8 with one scale per 128-element block ([V4-KERNEL] FP8
+ * block quantisation: scale = amax / 448 so the block fits E4M3's +-448;
+ * optional power-of-two scale; optional quantise-then-dequantise).
+ *
+ * Token t (0 <= t < T) goes to cache row c = t / rows_per_seq, slot
+ * p = positions[t]; a token whose p is outside [0, S_max) is skipped.  Two
+ * tokens of one row with the same position race (either may win).
+ *   DSA_KEY_FP8_E4M3: amax = max_d |k[t, d]|; s = amax / 448 (1 when
+ *     amax == 0), with DSA_CACHE_ROUND_SCALE the smallest power of two >= that;
+ *     code[d] = the E4M3 value nearest to clamp(k[t, d] / s, -448, 448), ties
+ *     to the even code (a negative value that rounds to zero gives -0); each
+ *     step is one binary32 operation, so the codes equal those of any exact
+ *     binary32 evaluation.  k_scale[c, p] = s.
+ *   DSA_KEY_BF16: the key as given; with DSA_CACHE_QDQ the bfloat16 nearest
+ *     to value(code[d]) * s (binary32 product) instead.
+ *
+ *   k_new     [T, 128] bf16, device
+ *   positions [T] int32, device
+ *   k_cache   [T / rows_per_seq, S_max, 128] bf16 or fp8 bytes, device, updated in place
+ *   k_scale   [T / rows_per_seq, S_max] fp32, device (fp8 only; must be NULL for bf16)
+ *
+ * Limits: D == 128; T >= 0 (T == 0 enqueues nothing, and k_new and
+ * positions may then be NULL); rows_per_seq >= 1 and
+ * T % rows_per_seq == 0; S_max >= 1; DSA_CACHE_QDQ only with a bf16 cache;
+ * DSA_CACHE_ROUND_SCALE only where a scale is computed (fp8, or bf16 with
+ * DSA_CACHE_QDQ).  k_new must not overlap the cache.  Inputs must be
+ * finite.
+ */
+dsa_status_t dsa_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
+                             const int32_t* positions, dsa_key_dtype_t k_dtype, void* k_cache, float* k_scale,
+                             int32_t S_max, uint32_t flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

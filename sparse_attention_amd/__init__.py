@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 DSA_KEY_BF16 = 0
 DSA_KEY_FP8_E4M3 = 1
 DSA_SCORE_RELU = 1
+DSA_CACHE_ROUND_SCALE = 1
+DSA_CACHE_QDQ = 2
 
 _STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED", 4: "DSA_ERR_ALIGN",
            5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_LAUNCH"}
@@ -80,6 +82,8 @@ def load_library(path: Optional[str] = None):
     lib.dsa_decode_step_workspace_size.argtypes = [ctypes.POINTER(_DecodeArgs)]
     lib.dsa_decode_step.restype = st
     lib.dsa_decode_step.argtypes = [ctypes.POINTER(_DecodeArgs), vp, sz, vp]
+    lib.dsa_cache_write.restype = st
+    lib.dsa_cache_write.argtypes = [vp, i32, i32, i32, vp, st, vp, vp, i32, u32, vp]
     if path is None:
         _lib = lib
     return lib
@@ -251,3 +255,27 @@ def dsa_decode_step(index_q, index_w, k_cache, **kw):
     step = DecodeStep(index_q, index_w, k_cache, **kw)
     step()
     return step
+
+
+def dsa_cache_write(k_new, positions, k_cache, *, k_scale=None, rows_per_seq: int = 1, round_scale: bool = False,
+                    qdq: bool = False) -> None:
+    """Store k_new [T, 128] bf16 into k_cache [T // rows_per_seq, S_max, 128] in place at positions [T] int32.
+
+    An fp8 cache (uint8 / float8_e4m3fn codes, with k_scale [n_seq, S_max] fp32) is written block-quantised;
+    a bf16 cache gets the key as is, or quantised and dequantised with ``qdq``."""
+    _dev(k_new, "k_new", (torch.bfloat16,))
+    _dev(positions, "positions", (torch.int32,))
+    _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
+    kd = _key_args(k_cache, k_scale)
+    if kd == DSA_KEY_FP8_E4M3 and k_scale is None:
+        raise ValueError("an fp8 key cache needs k_scale")
+    T, D = k_new.shape
+    n_seq, S_max = k_cache.shape[0], k_cache.shape[1]
+    if positions.shape != (T,) or k_cache.shape[2] != D or (T and n_seq * int(rows_per_seq) != T):
+        raise ValueError("shapes: k_new [T, D], positions [T], k_cache [T // rows_per_seq, S_max, D]")
+    if k_scale is not None and tuple(k_scale.shape) != (n_seq, S_max):
+        raise ValueError("k_scale must be [n_seq, S_max]")
+    flags = (DSA_CACHE_ROUND_SCALE if round_scale else 0) | (DSA_CACHE_QDQ if qdq else 0)
+    st = load_library().dsa_cache_write(_ptr(k_new), T, int(rows_per_seq), D, _ptr(positions), kd, _ptr(k_cache),
+                                        _ptr(k_scale), S_max, flags, _stream())
+    _check("dsa_cache_write", st)

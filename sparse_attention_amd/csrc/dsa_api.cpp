@@ -133,6 +133,25 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     return DSA_OK;
 }
 
+dsa_status_t check_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
+                               const int32_t* positions, dsa_key_dtype_t k_dtype, const void* k_cache,
+                               const float* k_scale, int32_t S_max, uint32_t flags)
+{
+    if (!k_cache || (T != 0 && (!k_new || !positions))) return DSA_ERR_NULL;
+    if (k_dtype != DSA_KEY_BF16 && k_dtype != DSA_KEY_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+    if (k_dtype == DSA_KEY_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+    if (k_dtype == DSA_KEY_BF16 && k_scale) return DSA_ERR_SHAPE;
+    if (T < 0 || rows_per_seq < 1 || S_max < 1 || T % rows_per_seq != 0) return DSA_ERR_SHAPE;
+    if (D != DSA_INDEX_HEAD_DIM) return DSA_ERR_UNSUPPORTED;
+    if (flags & ~(DSA_CACHE_ROUND_SCALE | DSA_CACHE_QDQ)) return DSA_ERR_UNSUPPORTED;
+    const bool qdq = (flags & DSA_CACHE_QDQ) != 0;
+    if (qdq && k_dtype != DSA_KEY_BF16) return DSA_ERR_UNSUPPORTED;
+    if ((flags & DSA_CACHE_ROUND_SCALE) && k_dtype == DSA_KEY_BF16 && !qdq) return DSA_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(k_cache) || !aligned16(positions) || (k_scale && !aligned16(k_scale)))
+        return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +275,18 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
     e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
                                 args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);
     return launch_status(e);
+}
+
+dsa_status_t dsa_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
+                             const int32_t* positions, dsa_key_dtype_t k_dtype, void* k_cache, float* k_scale,
+                             int32_t S_max, uint32_t flags, hipStream_t stream)
+{
+    const dsa_status_t s =
+        check_cache_write(k_new, T, rows_per_seq, D, positions, k_dtype, k_cache, k_scale, S_max, flags);
+    if (s != DSA_OK) return s;
+    return launch_status(dsa::launch_cache_write(k_new, T, rows_per_seq, positions, k_dtype == DSA_KEY_FP8_E4M3,
+                                                 (flags & DSA_CACHE_QDQ) != 0, (flags & DSA_CACHE_ROUND_SCALE) != 0,
+                                                 k_cache, k_scale, S_max, stream));
 }
 
 }  // extern "C"

@@ -17,13 +17,13 @@ hipError_t launch_score_decode(const void* q, const float* w, const void* k_cach
                                int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
                                size_t zero_words, hipStream_t stream);
 
-// Whether this build contains the prefill (per-head MFMA) scoring kernel.
 // Decode indexer score with a per-head activation (max(0, .)): per-head MFMA, H <= 64.
 hipError_t launch_score_decode_heads(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                      bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
                                      int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
                                      size_t zero_words, hipStream_t stream);
 
+// Whether this build contains the prefill (per-head MFMA) scoring kernel.
 bool score_prefill_available();
 
 // Prefill indexer score: rows_per_seq query rows share one bf16 cache; per-head MFMA.
@@ -51,5 +51,11 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_s
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                               int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
                               hipStream_t stream);
+
+// Key-cache write of T tokens (128 bf16 elements each): fp8 codes + scale,
+// bf16 copy, or bf16 quantised and dequantised (qdq).
+hipError_t launch_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, const int32_t* positions,
+                              bool key_fp8, bool qdq, bool round_scale, void* k_cache, float* k_scale,
+                              int32_t S_max, hipStream_t stream);
 
 }  // namespace dsa

@@ -155,3 +155,31 @@ def test_decode_step_validation(lib):
     a.struct_size = old
     a.window = -1
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE  # validation went on past the size
+
+
+def test_cache_write_validation(lib):
+    f = lib.dsa_cache_write
+    args = dict(k=_p(A), T=4, rps=1, D=128, pos=_p(A), kd=1, kc=_p(A), ks=_p(A), S=100, flags=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["k"], a["T"], a["rps"], a["D"], a["pos"], a["kd"], a["kc"], a["ks"], a["S"], a["flags"], None)
+
+    assert call(k=None) == ERR_NULL
+    assert call(pos=None) == ERR_NULL
+    assert call(kc=None) == ERR_NULL
+    assert call(ks=None) == ERR_NULL               # fp8 without scales
+    assert call(kd=0) == ERR_SHAPE                 # bf16 with scales
+    assert call(kd=5) == ERR_UNSUPPORTED
+    assert call(T=-1) == ERR_SHAPE
+    assert call(T=5, rps=2) == ERR_SHAPE
+    assert call(rps=0) == ERR_SHAPE
+    assert call(S=0) == ERR_SHAPE
+    assert call(D=256) == ERR_UNSUPPORTED
+    assert call(flags=4) == ERR_UNSUPPORTED
+    assert call(flags=2) == ERR_UNSUPPORTED        # quantise-dequantise needs a bf16 cache
+    assert call(kd=0, ks=None, flags=1) == ERR_UNSUPPORTED  # a plain bf16 copy computes no scale
+    assert call(k=_p(A + 8)) == ERR_ALIGN
+    assert call(pos=_p(A + 4)) == ERR_ALIGN
+    assert call(T=0) == OK                         # nothing to write: nothing is enqueued
+    assert call(T=0, k=None, pos=None) == OK       # (empty tensors may have no storage)

@@ -135,3 +135,25 @@ def test_fullsize_decode_step(dsa):
         live = lst[b][lst[b] >= 0]
         assert len(np.unique(live)) == len(live) and live.max() < nv[b]
         assert np.array_equal(lst[b, w.index_topk:], np.arange(nv[b] - w.window, nv[b]))
+
+
+def test_fullsize_fp8_cache_write():
+    """The long-context fp8 cache (4 x 131072 slots) quantised on the GPU from bf16 keys, in one call;
+    the oracle requantises 4096 sampled slots (first, last and random) and they must match bit for bit."""
+    import sparse_attention_amd as dsa
+
+    n_seq, S_max = 4, 131072
+    keys = synthetic.normal(41, 0, (n_seq * S_max, 128))
+    pos = np.tile(np.arange(S_max, dtype=np.int32), n_seq)
+    announce("dsa_cache_write fp8 full: %d x %d slots from bf16 keys (sampled check)" % (n_seq, S_max))
+    kc = torch.empty((n_seq, S_max, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((n_seq, S_max), dtype=torch.float32, device="cuda")
+    dsa.dsa_cache_write(keys.cuda(), torch.from_numpy(pos).cuda(), kc, k_scale=ks, rows_per_seq=S_max)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(42)
+    rows = np.unique(np.concatenate([[0, S_max - 1, n_seq * S_max - 1], g.integers(0, n_seq * S_max, 4093)]))
+    want_c, want_s = oracle.quantize_fp8_blocks(keys[torch.from_numpy(rows)])
+    got_c = kc.view(-1, 128)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    got_s = ks.view(-1)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_s, want_s[:, 0])
