@@ -173,9 +173,10 @@ def dsa_topk(scores, index_topk: int, *, positions=None, valid_len: int = -1, wi
     return (idx, tsc) if with_scores else idx
 
 
-def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False):
+def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False, out=None):
     """Sparse MQA with sink.  q [B, S, Hq, Dqk] bf16; kv [B, S_kv, Dqk] bf16; attn_sink [Hq] fp32 or None;
-    topk_idx [B, S, K_top] int32.  Returns out [B, S, Hq, dv] bf16 (and lse [B, S, Hq] fp32)."""
+    topk_idx [B, S, K_top] int32.  Returns out [B, S, Hq, dv] bf16 (and lse [B, S, Hq] fp32); `out` may be
+    given."""
     _dev(q, "q", (torch.bfloat16,))
     _dev(kv, "kv", (torch.bfloat16,))
     _dev(topk_idx, "topk_idx", (torch.int32,))
@@ -185,7 +186,11 @@ def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, wit
     S_kv = kv.shape[1]
     K_top = topk_idx.shape[2]
     lib = load_library()
-    out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    if out is None:
+        out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", (torch.bfloat16,))
+    if tuple(out.shape) != (B, S, Hq, dv):
+        raise ValueError("out must be [B, S, Hq, dv]")
     lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device) if with_lse else None
     nws = lib.dsa_sparse_attn_workspace_size(B, S, Hq, int(dv), K_top)
     ws = _workspace(nws, q.device)

@@ -8,6 +8,7 @@ indexer consumes).  Every element is a pure function of
 can be regenerated on its own.
 """
 from .gen import (  # noqa: F401
+    causal_index_lists,
     normal,
     quantize_fp8_blocks,
     uniform_int,

@@ -71,6 +71,29 @@ def uniform_int(seed: int, tensor_id: int, n: int, lo: int, hi: int) -> torch.Te
     return torch.from_numpy(g.integers(lo, hi, size=n, endpoint=True, dtype=np.int64).astype(np.int32))
 
 
+def causal_index_lists(seed: int, tensor_id: int, S: int, k: int, *, rows=None) -> torch.Tensor:
+    """Per-query index lists shaped like a causal top-k: row i holds min(k, i + 1)
+    distinct slots drawn uniformly from [0, i] (all of them when i < k), in random
+    order, then -1 padding.  int32 [len(rows), k]; row i is drawn from stream
+    (seed, tensor_id, i)."""
+    rows = list(range(S)) if rows is None else [int(r) for r in rows]
+    out = np.full((len(rows), k), -1, dtype=np.int32)
+
+    def work(j):
+        i = rows[j]
+        g = _stream(seed, tensor_id, i)
+        n = min(k, i + 1)
+        out[j, :n] = g.permutation(i + 1)[:n] if i + 1 <= 4 * k else g.choice(i + 1, size=n, replace=False)
+
+    if len(rows) > 64:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(work, range(len(rows))))
+    else:
+        for j in range(len(rows)):
+            work(j)
+    return torch.from_numpy(out)
+
+
 def quantize_fp8_blocks(x: torch.Tensor):
     """Store x [..., D] as OCP FP8 E4M3 codes with one fp32 scale per last-axis block.
 

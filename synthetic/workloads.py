@@ -1,4 +1,5 @@
-"""The five DSA workloads (shapes and value distributions), at full size or scaled down.
+"""The five DSA workloads (shapes and value distributions), at full size or scaled down,
+plus prefill-shaped sparse attention (the prefill workload's top-k lists feeding attention).
 
 Every recipe takes its shape parameters as keyword arguments, defaulting to
 the full-size workload; tests pass smaller values to get the same structure
@@ -16,9 +17,9 @@ from typing import Optional
 
 import torch
 
-from .gen import normal, quantize_fp8_blocks, uniform_int
+from .gen import causal_index_lists, normal, quantize_fp8_blocks, uniform_int
 
-T_INDEX_Q, T_INDEX_W, T_KCACHE, T_POS, T_Q, T_KV, T_SINK = 1, 2, 3, 4, 5, 6, 7
+T_INDEX_Q, T_INDEX_W, T_KCACHE, T_POS, T_Q, T_KV, T_SINK, T_LIST = 1, 2, 3, 4, 5, 6, 7, 8
 
 SEED_BASE = 0xD5A00000
 
@@ -44,6 +45,7 @@ class Workload:
     sink: Optional[torch.Tensor] = None  # [Hq] fp32
     sm_scale: float = 0.0
     dv: int = 0
+    index_list: Optional[torch.Tensor] = None  # [B, S, K_top] int32 (attention-only workloads)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -144,12 +146,29 @@ def full_decode_step(seed=SEED_BASE + 5, *, B=64, H=64, D=128, S_max=65536, topk
         sm_scale=Dqk ** -0.5, dv=Dv)
 
 
+def prefill_attn(seed=SEED_BASE + 6, *, S=8192, topk=2048, Hq=128, Dqk=576, Dv=512, kv_sigma=0.5) -> Workload:
+    """Prefill-shaped sparse attention: one sequence of S = 8192 query tokens, each attending to
+    its own causal top-2048 list (min(2048, i + 1) distinct slots of [0, i], -1 padded), with the
+    attention of the full decode step (128 heads, qk 576 / v 512, KV N(0, 0.5), per-head sink).
+    Attention only: the indexer fields are None."""
+    return Workload(
+        name="prefill_attn", seed=seed,
+        index_q=None, index_w=None, k_cache=None, k_scale=None, positions=None, valid_len=-1,
+        rows_per_seq=S, index_scale=0.0, index_topk=topk,
+        q=normal(seed, T_Q, (1, S, Hq, Dqk)),
+        kv=normal(seed, T_KV, (1, S, Dqk), sigma=kv_sigma),
+        sink=normal(seed, T_SINK, (Hq,), dtype=torch.float32),
+        sm_scale=Dqk ** -0.5, dv=Dv,
+        index_list=causal_index_lists(seed, T_LIST, S, topk).view(1, S, topk))
+
+
 WORKLOADS = {
     "tiny_decode": tiny_decode,
     "batched_decode": batched_decode,
     "prefill": prefill,
     "fp8_long_decode": fp8_long_decode,
     "full_decode_step": full_decode_step,
+    "prefill_attn": prefill_attn,
 }
 
 

@@ -157,3 +157,20 @@ def test_fullsize_fp8_cache_write():
     got_s = ks.view(-1)[torch.from_numpy(rows).cuda()].cpu().numpy()
     assert np.array_equal(got_c, want_c)
     assert np.array_equal(got_s, want_s[:, 0])
+
+
+def test_fullsize_prefill_attn(dsa):
+    """Prefill-shaped sparse attention at full size (8192 queries, causal top-2048 lists, 128 heads,
+    576 / 512), in bench.py's launch configuration; the oracle recomputes sampled query tokens."""
+    w = synthetic.make_workload("prefill_attn")
+    S = w.q.shape[1]
+    announce("prefill_attn full: %d queries x top-%d, 128 heads, 576/512 (sampled tokens)" % (S, w.index_topk))
+    out = dsa.dsa_sparse_attn(_cuda(w.q), _cuda(w.kv), _cuda(w.sink), _cuda(w.index_list), sm_scale=w.sm_scale,
+                              dv=w.dv)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(61)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 2047, 2048, 4095, S - 1], g.integers(0, S, 8)]))
+    sl = torch.from_numpy(rows)
+    ref, _ = oracle.sparse_attn(w.q[:, sl], w.kv, w.sink, w.index_list[:, sl], sm_scale=w.sm_scale, dv=w.dv)
+    check_attn(out[:, sl.cuda()].float().cpu().numpy(), ref)
+    assert bool(torch.isfinite(out.float()).all())

@@ -280,6 +280,15 @@ def test_attn_peaked_softmax(dsa):
     assert rel < 2e-2
 
 
+# Prefill-shaped attention: many query tokens of one sequence, each with its own causal list
+@pytest.mark.parametrize("S,topk,Hq,Dqk,Dv", [(200, 128, 128, 576, 512), (300, 64, 16, 192, 128),
+                                              (130, 100, 24, 128, 96)])
+def test_attn_prefill_causal_lists(dsa, S, topk, Hq, Dqk, Dv):
+    w = synthetic.make_workload("prefill_attn", S=S, topk=topk, Hq=Hq, Dqk=Dqk, Dv=Dv)
+    _, rel = _attn_case(dsa, "prefill causal lists", w.q, w.kv, w.sink, w.index_list, w.sm_scale, Dv)
+    assert rel < 2e-2
+
+
 # ------------------------------------------------------------------ decode step
 
 def _decode_case(dsa, w, label, relu=False):
