@@ -9,6 +9,9 @@
  *                     with the always-selected sliding window
  *   dsa_cache_write   new keys stored in the key cache at their positions,
  *                     optionally FP8 block-quantised
+ *   dsa_index_score_paged, dsa_sparse_attn_paged
+ *                     the decode scorer and the attention over paged caches
+ *                     (a block table into a shared page pool)
  *
  * Sources (web pages, cited by title and section):
  *   [NKI-V32]   AWS Neuron "DeepSeek-V3.2 Sparse Indexer Kernel API Reference"
@@ -17,6 +20,8 @@
  *               "nemo_automodel.components.models.deepseek_v4.optimized_kernels"
  *   [V4-KERNEL] kwkr.cn article on DeepSeek-V4-Pro-0813-nvfp4-DSpark
  *               inference/kernel.py (sparse-attention and FP8 sections)
+ *   [TOKAMAX]   OpenXLA tokamax "Supported Ops and Hardware", Attention
+ *               Variants table (lightning_indexer, batched_rpa rows)
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE memory on the current HIP device, owned by
@@ -175,6 +180,29 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Paged caches ([TOKAMAX] lightning_indexer scores over a paged KV cache;
+ * batched_rpa attends over one).  A sequence's slots are cut into runs of
+ * page_size consecutive slots; run p of sequence r lives in page
+ * block_table[r * max_pages + p] of a pool shared by all sequences, so
+ * slot s of sequence r is pool row
+ *   block_table[r * max_pages + s / page_size] * page_size + s % page_size.
+ * Pools: keys [n_pages * page_size, 128] (bf16, or fp8 codes with scales
+ * [n_pages * page_size] fp32), KV [n_pages * page_size, Dqk] bf16.
+ * Table entries for slots a call reads must lie in [0, n_pages); an entry
+ * outside it is clamped into the pool (wrong data, no fault).
+ *
+ * Limits: page_size a power of two, 64 <= page_size <= 65536;
+ * max_pages >= 1; n_pages >= 1; n_pages * page_size < 2^31; the logical
+ * slot range (S_max, S_kv) at most max_pages * page_size.
+ */
+typedef struct dsa_paged_cache {
+    const int32_t* block_table; /* [n_seq, max_pages] int32, device */
+    int32_t max_pages;          /* columns of block_table */
+    int32_t page_size;          /* slots per page */
+    int32_t n_pages;            /* pages in the pool */
+} dsa_paged_cache_t;
+
+/*
  * dsa_decode_step -- one DSA decode step for B sequences (one query token
  * each): indexer score of every cached slot -> top-k -> index list =
  * top-k plus the always-selected window of the last `window` attendable
@@ -185,8 +213,12 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
  * the kv slot s are the same position, so S_kv == S_max.
  *
  * The struct is versioned by struct_size (set it to sizeof(dsa_decode_args_t));
- * a struct_size that ends before index_flags is accepted, and the flags are
- * then 0.
+ * fields added later read as 0 / NULL when struct_size ends before them
+ * (the oldest accepted size ends before index_flags).
+ *
+ * With paging != NULL, k_cache / k_scale and kv are page pools (see
+ * dsa_paged_cache_t) sharing one block table, and S_max is the logical slot
+ * count of every sequence.
  */
 typedef struct dsa_decode_args {
     size_t struct_size;
@@ -215,11 +247,32 @@ typedef struct dsa_decode_args {
     int32_t* index_list;        /* [B, index_topk + window] int32 or NULL (then workspace) */
     /* added later; a struct_size that ends before this field reads as 0 */
     uint32_t index_flags;       /* flags of dsa_index_score (DSA_SCORE_RELU: H <= 64) */
+    const dsa_paged_cache_t* paging; /* NULL: contiguous caches */
 } dsa_decode_args_t;
 
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args);
 dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+
+/* dsa_index_score over a paged key cache, one query row per sequence
+ * (rows_per_seq = 1); arguments and results as dsa_index_score, with
+ * k_cache / k_scale the page pools and S_max the logical slot count of
+ * every sequence (the width of scores). */
+dsa_status_t dsa_index_score_paged(const void* q, const float* w, const void* k_pool, const float* k_scale_pool,
+                                   dsa_key_dtype_t k_dtype, const dsa_paged_cache_t* paging,
+                                   const int32_t* positions, int32_t valid_len, int32_t M, int32_t H, int32_t D,
+                                   int32_t S_max, float scale, uint32_t flags, float* scores, hipStream_t stream);
+
+/* dsa_sparse_attn over a paged KV pool: topk_idx holds logical slots of
+ * each sequence (masked unless 0 <= slot < S_kv), looked up through the
+ * block table; the pool itself has no 2 GiB limit.  Workspace as for
+ * dsa_sparse_attn (same size query). */
+dsa_status_t dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* attn_sink,
+                                   const int32_t* topk_idx, const dsa_paged_cache_t* paging, int32_t B, int32_t S,
+                                   int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* flags of dsa_cache_write */
 #define DSA_CACHE_ROUND_SCALE 1u /* power-of-two scale: the smallest 2^e >= amax / 448 */

@@ -15,6 +15,7 @@ Functions follow the web pages cited in ``dsa_oracle.c``:
   * ``quantize_fp8_blocks`` / ``dequantize_fp8_blocks`` -- FP8 E4M3 block
                         quantiser (binary32 decisions, nearest code, ties even)
   * ``cache_write``  -- new keys stored at their positions, optionally quantised
+  * ``unpage``       -- a paged pool read back as contiguous per-sequence caches
 """
 from __future__ import annotations
 
@@ -303,3 +304,33 @@ def cache_write(k_new, positions, k_cache, k_scale=None, *, rows_per_seq: int = 
         else:
             cache[c, p] = vals[t]
     return (cache, scales) if fp8 else cache
+
+
+# ------------------------------------------------------------- paged caches
+
+def unpage(pool, block_table, page_size: int, n_slots: int) -> np.ndarray:
+    """Contiguous [n_seq, n_slots, ...] view of a page pool [n_pages * page_size, ...]: slot s of
+    sequence r is pool row block_table[r, s // page_size] * page_size + s % page_size
+    (tokamax "Supported Ops and Hardware", lightning_indexer over a paged KV cache)."""
+    try:
+        import torch
+
+        if isinstance(pool, torch.Tensor):
+            pool = pool.detach().cpu()
+            if pool.dtype == torch.bfloat16:
+                pool = pool.view(torch.int16).numpy().view(np.uint16)
+            elif pool.dtype == torch.float8_e4m3fn:
+                pool = pool.view(torch.uint8).numpy()
+            else:
+                pool = pool.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    bt = _np(block_table, np.int64)
+    n_seq = bt.shape[0]
+    out = np.empty((n_seq, n_slots) + pool.shape[1:], pool.dtype)
+    for r in range(n_seq):
+        for s in range(0, n_slots, page_size):
+            n = min(page_size, n_slots - s)
+            base = bt[r, s // page_size] * page_size
+            out[r, s:s + n] = pool[base:base + n]
+    return out

@@ -46,8 +46,24 @@ class _DecodeArgs(ctypes.Structure):
         ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("attn_sink", ctypes.c_void_p),
         ("Hq", ctypes.c_int32), ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("scores", ctypes.c_void_p),
-        ("index_list", ctypes.c_void_p), ("index_flags", ctypes.c_uint32),
+        ("index_list", ctypes.c_void_p), ("index_flags", ctypes.c_uint32), ("paging", ctypes.c_void_p),
     ]
+
+
+class _PagedCache(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
+
+
+class Paging:
+    """A paged cache layout: block_table [n_seq, max_pages] int32 on the GPU, page_size slots per page,
+    n_pages pages in the pool.  Pools are [n_pages * page_size, ...] tensors."""
+
+    def __init__(self, block_table: torch.Tensor, page_size: int, n_pages: int):
+        _dev(block_table, "block_table", (torch.int32,))
+        self.block_table = block_table
+        self.page_size, self.n_pages = int(page_size), int(n_pages)
+        self.struct = _PagedCache(block_table.data_ptr(), int(block_table.shape[1]), self.page_size, self.n_pages)
 
 
 _lib = None
@@ -82,6 +98,12 @@ def load_library(path: Optional[str] = None):
     lib.dsa_decode_step_workspace_size.argtypes = [ctypes.POINTER(_DecodeArgs)]
     lib.dsa_decode_step.restype = st
     lib.dsa_decode_step.argtypes = [ctypes.POINTER(_DecodeArgs), vp, sz, vp]
+    pp = ctypes.POINTER(_PagedCache)
+    lib.dsa_index_score_paged.restype = st
+    lib.dsa_index_score_paged.argtypes = [vp, vp, vp, vp, st, pp, vp, i32, i32, i32, i32, i32, f32, u32, vp, vp]
+    lib.dsa_sparse_attn_paged.restype = st
+    lib.dsa_sparse_attn_paged.argtypes = [vp, vp, vp, vp, pp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz,
+                                          vp]
     lib.dsa_cache_write.restype = st
     lib.dsa_cache_write.argtypes = [vp, i32, i32, i32, vp, st, vp, vp, i32, u32, vp]
     if path is None:
@@ -135,9 +157,12 @@ def _key_args(k_cache: torch.Tensor, k_scale: Optional[torch.Tensor]):
 
 
 def dsa_index_score(q, w, k_cache, *, scale: float, k_scale=None, positions=None, valid_len: int = -1,
-                    rows_per_seq: int = 1, relu: bool = False, out=None) -> torch.Tensor:
+                    rows_per_seq: int = 1, relu: bool = False, out=None, paging: Optional[Paging] = None,
+                    s_max: Optional[int] = None) -> torch.Tensor:
     """Indexer scores [M, S_max] fp32.  q [M, H, 128] bf16; w [M, H] fp32;
-    k_cache [M // rows_per_seq, S_max, 128] bf16 or uint8/float8_e4m3fn codes (+ k_scale [n_seq, S_max])."""
+    k_cache [M // rows_per_seq, S_max, 128] bf16 or uint8/float8_e4m3fn codes (+ k_scale [n_seq, S_max]).
+    With ``paging`` (decode rows only), k_cache / k_scale are page pools [n_pages * page_size, ...] and
+    ``s_max`` is the logical slot count of every sequence."""
     _dev(q, "q", (torch.bfloat16,))
     _dev(w, "w", (torch.float32,))
     _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -145,13 +170,25 @@ def dsa_index_score(q, w, k_cache, *, scale: float, k_scale=None, positions=None
     if positions is not None:
         _dev(positions, "positions", (torch.int32,))
     M, H, D = q.shape
-    S_max = k_cache.shape[1]
+    if paging is not None:
+        if s_max is None or rows_per_seq != 1:
+            raise ValueError("paged scoring needs s_max and one row per sequence")
+        S_max = int(s_max)
+    else:
+        S_max = k_cache.shape[1]
     if out is None:
         out = torch.empty((M, S_max), dtype=torch.float32, device=q.device)
     _dev(out, "out", (torch.float32,))
-    st = load_library().dsa_index_score(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), kd, _ptr(positions),
-                                        int(valid_len), M, int(rows_per_seq), H, D, S_max, float(scale),
-                                        DSA_SCORE_RELU if relu else 0, _ptr(out), _stream())
+    flags = DSA_SCORE_RELU if relu else 0
+    lib = load_library()
+    if paging is not None:
+        st = lib.dsa_index_score_paged(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), kd, ctypes.byref(paging.struct),
+                                       _ptr(positions), int(valid_len), M, H, D, S_max, float(scale), flags, _ptr(out),
+                                       _stream())
+        _check("dsa_index_score_paged", st)
+        return out
+    st = lib.dsa_index_score(_ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), kd, _ptr(positions), int(valid_len), M,
+                             int(rows_per_seq), H, D, S_max, float(scale), flags, _ptr(out), _stream())
     _check("dsa_index_score", st)
     return out
 
@@ -173,17 +210,21 @@ def dsa_topk(scores, index_topk: int, *, positions=None, valid_len: int = -1, wi
     return (idx, tsc) if with_scores else idx
 
 
-def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False, out=None):
+def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False, out=None,
+                    paging: Optional[Paging] = None, s_kv: Optional[int] = None):
     """Sparse MQA with sink.  q [B, S, Hq, Dqk] bf16; kv [B, S_kv, Dqk] bf16; attn_sink [Hq] fp32 or None;
     topk_idx [B, S, K_top] int32.  Returns out [B, S, Hq, dv] bf16 (and lse [B, S, Hq] fp32); `out` may be
-    given."""
+    given.  With ``paging``, kv is a page pool [n_pages * page_size, Dqk] and ``s_kv`` the logical slot
+    count of every sequence."""
     _dev(q, "q", (torch.bfloat16,))
     _dev(kv, "kv", (torch.bfloat16,))
     _dev(topk_idx, "topk_idx", (torch.int32,))
     if attn_sink is not None:
         _dev(attn_sink, "attn_sink", (torch.float32,))
     B, S, Hq, Dqk = q.shape
-    S_kv = kv.shape[1]
+    if paging is not None and s_kv is None:
+        raise ValueError("paged attention needs s_kv")
+    S_kv = int(s_kv) if paging is not None else kv.shape[1]
     K_top = topk_idx.shape[2]
     lib = load_library()
     if out is None:
@@ -194,9 +235,15 @@ def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, wit
     lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device) if with_lse else None
     nws = lib.dsa_sparse_attn_workspace_size(B, S, Hq, int(dv), K_top)
     ws = _workspace(nws, q.device)
-    st = lib.dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idx), B, S, Hq, Dqk, int(dv), S_kv, K_top,
-                             float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream())
-    _check("dsa_sparse_attn", st)
+    if paging is not None:
+        st = lib.dsa_sparse_attn_paged(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idx), ctypes.byref(paging.struct),
+                                       B, S, Hq, Dqk, int(dv), S_kv, K_top, float(sm_scale), _ptr(out), _ptr(lse),
+                                       _ptr(ws), nws, _stream())
+        _check("dsa_sparse_attn_paged", st)
+    else:
+        st = lib.dsa_sparse_attn(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idx), B, S, Hq, Dqk, int(dv), S_kv,
+                                 K_top, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream())
+        _check("dsa_sparse_attn", st)
     return (out, lse) if with_lse else out
 
 
@@ -205,7 +252,8 @@ class DecodeStep:
 
     def __init__(self, index_q, index_w, k_cache, *, positions=None, valid_len: int = -1, index_scale: float,
                  index_topk: int, window: int, q, kv, attn_sink, sm_scale: float, dv: int, k_scale=None,
-                 keep_scores: bool = True, keep_index_list: bool = True, relu: bool = False):
+                 keep_scores: bool = True, keep_index_list: bool = True, relu: bool = False,
+                 paging: Optional[Paging] = None, s_max: Optional[int] = None):
         _dev(index_q, "index_q", (torch.bfloat16,))
         _dev(index_w, "index_w", (torch.float32,))
         _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -217,7 +265,9 @@ class DecodeStep:
             _dev(attn_sink, "attn_sink", (torch.float32,))
         kd = _key_args(k_cache, k_scale)
         B, H, _ = index_q.shape
-        S_max = k_cache.shape[1]
+        if paging is not None and s_max is None:
+            raise ValueError("a paged decode step needs s_max")
+        S_max = int(s_max) if paging is not None else k_cache.shape[1]
         _, S, Hq, Dqk = q.shape
         if S != 1:
             raise ValueError("decode step takes one query token per sequence")
@@ -227,7 +277,7 @@ class DecodeStep:
         self.scores = torch.empty((B, S_max), dtype=torch.float32, device=dev) if keep_scores else None
         self.index_list = (torch.empty((B, index_topk + window), dtype=torch.int32, device=dev)
                            if keep_index_list else None)
-        self._keep = (index_q, index_w, k_cache, k_scale, positions, q, kv, attn_sink)
+        self._keep = (index_q, index_w, k_cache, k_scale, positions, q, kv, attn_sink, paging)
         a = _DecodeArgs()
         a.struct_size = ctypes.sizeof(_DecodeArgs)
         a.index_q, a.index_w, a.k_cache = index_q.data_ptr(), index_w.data_ptr(), k_cache.data_ptr()
@@ -243,6 +293,7 @@ class DecodeStep:
         a.scores = None if self.scores is None else self.scores.data_ptr()
         a.index_list = None if self.index_list is None else self.index_list.data_ptr()
         a.index_flags = DSA_SCORE_RELU if relu else 0
+        a.paging = None if paging is None else ctypes.addressof(paging.struct)
         self._args = a
         lib = load_library()
         self._nws = lib.dsa_decode_step_workspace_size(ctypes.byref(a))

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dsa_internal.h"
+
 namespace dsa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -87,6 +89,22 @@ __device__ __forceinline__ uint32_t f32_order_key(float f)
 {
     uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Where slot s of sequence r lives in a key or KV store: row r * S_max + s of
+// a contiguous [n_seq, S_max] store, or, for a page pool, row
+// page * P + (s mod P) with page = block_table[r][s / P] (P = 2^lp slots per
+// page).  A page id outside [0, n_pages) is clamped into the pool, so a bad
+// table reads wrong rows but never leaves the allocation.
+template <bool PAGED>
+__device__ __forceinline__ size_t store_row(const PageMap& pm, int r, int s, int S_max)
+{
+    if (!PAGED) return (size_t)r * S_max + s;
+    // callers may ask for slots past the sequence's last page (rounds that load
+    // nothing): the table column is clamped too, so the table read stays in bounds
+    const int col = min(s >> pm.lp, pm.max_pages - 1);
+    const uint32_t page = min((uint32_t)pm.table[(size_t)r * pm.max_pages + col], (uint32_t)(pm.n_pages - 1));
+    return ((size_t)page << pm.lp) | (uint32_t)(s & ((1 << pm.lp) - 1));
 }
 
 // Grid-stride clear of an unrelated buffer riding along with a 2-D launch

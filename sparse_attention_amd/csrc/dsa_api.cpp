@@ -58,15 +58,32 @@ dsa_status_t check_topk(const float* scores, int32_t M, int32_t S_max, int32_t k
 }
 
 dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t B, int32_t S, int32_t Hq,
-                               int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, const void* out)
+                               int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, const void* out, bool paged = false)
 {
     if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
     if (B < 1 || S < 1 || Hq < 1 || S_kv < 1 || K_top < 1) return DSA_ERR_SHAPE;
     if (Dqk < 32 || Dqk > DSA_MAX_ATTN_DIM || Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (Dv < 16 || Dv > Dqk || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if ((long long)B * S > 65535) return DSA_ERR_SHAPE;
-    if ((long long)S_kv * Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's KV rows: 32-bit offsets
+    if (!paged && (long long)S_kv * Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's KV: 32-bit offsets
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+}
+
+// A paged-cache descriptor covering n_slots logical slots per sequence, as
+// the kernels' page map.
+dsa_status_t check_paging(const dsa_paged_cache_t* pg, int32_t n_slots, dsa::PageMap* pm)
+{
+    if (!pg || !pg->block_table) return DSA_ERR_NULL;
+    const int32_t P = pg->page_size;
+    if (P < 64 || P > 65536 || (P & (P - 1)) != 0) return DSA_ERR_UNSUPPORTED;
+    if (pg->max_pages < 1 || pg->n_pages < 1) return DSA_ERR_SHAPE;
+    if ((long long)pg->n_pages * P > INT32_MAX) return DSA_ERR_SHAPE;  // pool rows: 31-bit indices
+    if ((long long)n_slots > (long long)pg->max_pages * P) return DSA_ERR_SHAPE;
+    if (!aligned16(pg->block_table)) return DSA_ERR_ALIGN;
+    int lp = 0;
+    while ((1 << lp) < P) ++lp;
+    *pm = dsa::PageMap{pg->block_table, pg->max_pages, lp, pg->n_pages};
     return DSA_OK;
 }
 
@@ -99,10 +116,14 @@ decode_layout layout_decode(const dsa_decode_args_t* a)
     return L;
 }
 
-// index_flags, or 0 for a struct that ends before the field
+// index_flags / paging, or 0 / NULL for a struct that ends before the field
 uint32_t decode_flags(const dsa_decode_args_t* a)
 {
     return a->struct_size >= offsetof(dsa_decode_args_t, index_flags) + sizeof(uint32_t) ? a->index_flags : 0u;
+}
+const dsa_paged_cache_t* decode_paging(const dsa_decode_args_t* a)
+{
+    return a->struct_size >= offsetof(dsa_decode_args_t, paging) + sizeof(void*) ? a->paging : nullptr;
 }
 
 dsa_status_t check_decode(const dsa_decode_args_t* a)
@@ -123,7 +144,13 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     if (a->Hq < 1) return DSA_ERR_SHAPE;
     if (a->Dqk < 32 || a->Dqk > DSA_MAX_ATTN_DIM || a->Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
-    if ((long long)a->S_max * a->Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // KV rows: 32-bit offsets
+    if (decode_paging(a)) {
+        dsa::PageMap pm;
+        const dsa_status_t ps = check_paging(decode_paging(a), a->S_max, &pm);
+        if (ps != DSA_OK) return ps;
+    } else if ((long long)a->S_max * a->Dqk * 2 > INT32_MAX) {
+        return DSA_ERR_SHAPE;  // one sequence's KV rows: 32-bit offsets
+    }
     if (!aligned16(a->index_q) || !aligned16(a->index_w) || !aligned16(a->k_cache) || !aligned16(a->q) ||
         !aligned16(a->kv) || !aligned16(a->out))
         return DSA_ERR_ALIGN;
@@ -184,10 +211,11 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
     if (rows_per_seq == 1 && (flags & DSA_SCORE_RELU))
         return launch_status(dsa::launch_score_decode_heads(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3,
                                                             positions, valid_len, M, H, S_max, scale, scores, nullptr, 0,
-                                                            stream));
+                                                            nullptr, stream));
     if (rows_per_seq == 1)
         return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
-                                                      valid_len, M, H, S_max, scale, scores, nullptr, 0, stream));
+                                                      valid_len, M, H, S_max, scale, scores, nullptr, 0, nullptr,
+                                                      stream));
     return launch_status(dsa::launch_score_prefill(q, w, k_cache, positions, valid_len, M, rows_per_seq, H, S_max,
                                                    scale, (flags & DSA_SCORE_RELU) != 0, scores, stream));
 }
@@ -228,12 +256,12 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
     return launch_status(dsa::launch_sparse_attn(q, kv, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale,
-                                                 out, lse, workspace, stream));
+                                                 out, lse, workspace, nullptr, stream));
 }
 
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args)
 {
-    if (!args || args->struct_size < sizeof(dsa_decode_args_t) || args->B < 1 || args->S_max < 1 ||
+    if (!args || args->struct_size < offsetof(dsa_decode_args_t, index_flags) || args->B < 1 || args->S_max < 1 ||
         args->index_topk < 1 || args->window < 0 || args->Hq < 1 || args->Dv < 1)
         return 0;
     return layout_decode(args).total;
@@ -254,6 +282,12 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
     const int32_t K_top = args->index_topk + args->window;
 
     const bool relu = (decode_flags(args) & DSA_SCORE_RELU) != 0;
+    dsa::PageMap pm_store;
+    const dsa::PageMap* pm = nullptr;
+    if (decode_paging(args)) {
+        check_paging(decode_paging(args), args->S_max, &pm_store);  // validated by check_decode
+        pm = &pm_store;
+    }
     hipError_t e;
     // either scorer also clears the top-k workspace header, saving a launch
     if (relu) {
@@ -261,20 +295,56 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
                                            args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
                                            args->B, args->H, args->S_max, args->index_scale, scores,
                                            static_cast<uint32_t*>(topk_ws),
-                                           dsa::topk_header_words(args->B, args->S_max), stream);
+                                           dsa::topk_header_words(args->B, args->S_max), pm, stream);
     } else {
         e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
                                      args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len, args->B,
                                      args->H, args->S_max, args->index_scale, scores, static_cast<uint32_t*>(topk_ws),
-                                     dsa::topk_header_words(args->B, args->S_max), stream);
+                                     dsa::topk_header_words(args->B, args->S_max), pm, stream);
     }
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
                          args->window, list, nullptr, topk_ws, true, stream);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_sparse_attn(args->q, args->kv, args->attn_sink, list, args->B, 1, args->Hq, args->Dqk, args->Dv,
-                                args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, stream);
+                                args->S_max, K_top, args->sm_scale, args->out, args->lse, attn_ws, pm, stream);
     return launch_status(e);
+}
+
+dsa_status_t dsa_index_score_paged(const void* q, const float* w, const void* k_pool, const float* k_scale_pool,
+                                   dsa_key_dtype_t k_dtype, const dsa_paged_cache_t* paging,
+                                   const int32_t* positions, int32_t valid_len, int32_t M, int32_t H, int32_t D,
+                                   int32_t S_max, float scale, uint32_t flags, float* scores, hipStream_t stream)
+{
+    dsa_status_t s = check_index_score(q, w, k_pool, k_scale_pool, k_dtype, M, 1, H, D, S_max, flags, scores);
+    if (s != DSA_OK) return s;
+    dsa::PageMap pm;
+    s = check_paging(paging, S_max, &pm);
+    if (s != DSA_OK) return s;
+    const bool fp8 = k_dtype == DSA_KEY_FP8_E4M3;
+    if (flags & DSA_SCORE_RELU)
+        return launch_status(dsa::launch_score_decode_heads(q, w, k_pool, k_scale_pool, fp8, positions, valid_len, M,
+                                                            H, S_max, scale, scores, nullptr, 0, &pm, stream));
+    return launch_status(dsa::launch_score_decode(q, w, k_pool, k_scale_pool, fp8, positions, valid_len, M, H, S_max,
+                                                  scale, scores, nullptr, 0, &pm, stream));
+}
+
+dsa_status_t dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* attn_sink,
+                                   const int32_t* topk_idx, const dsa_paged_cache_t* paging, int32_t B, int32_t S,
+                                   int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
+{
+    dsa_status_t s = check_sparse_attn(q, kv_pool, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, out, true);
+    if (s != DSA_OK) return s;
+    dsa::PageMap pm;
+    s = check_paging(paging, S_kv, &pm);
+    if (s != DSA_OK) return s;
+    const size_t need = dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
+    return launch_status(dsa::launch_sparse_attn(q, kv_pool, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top,
+                                                 sm_scale, out, lse, workspace, &pm, stream));
 }
 
 dsa_status_t dsa_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,

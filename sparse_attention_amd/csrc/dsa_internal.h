@@ -9,19 +9,28 @@
 
 namespace dsa {
 
+// Page pool addressing of a paged key or KV store: slot s of sequence r is
+// row page * 2^lp + (s mod 2^lp) of the pool, page = table[r * max_pages + (s >> lp)].
+struct PageMap {
+    const int32_t* table;  // [n_seq, max_pages] device
+    int32_t max_pages;
+    int32_t lp;       // log2(page size)
+    int32_t n_pages;  // pages in the pool
+};
+
 // Decode indexer score, one row per sequence (phi = identity).  If zero_words
 // > 0 the launch also clears zero_ptr[0 .. zero_words) (the top-k workspace
 // header of a fused decode step).
 hipError_t launch_score_decode(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
                                int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
-                               size_t zero_words, hipStream_t stream);
+                               size_t zero_words, const PageMap* paging, hipStream_t stream);
 
 // Decode indexer score with a per-head activation (max(0, .)): per-head MFMA, H <= 64.
 hipError_t launch_score_decode_heads(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                      bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
                                      int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
-                                     size_t zero_words, hipStream_t stream);
+                                     size_t zero_words, const PageMap* paging, hipStream_t stream);
 
 // Whether this build contains the prefill (per-head MFMA) scoring kernel.
 bool score_prefill_available();
@@ -50,7 +59,7 @@ size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, i
 hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                               int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
-                              hipStream_t stream);
+                              const PageMap* paging, hipStream_t stream);
 
 // Key-cache write of T tokens (128 bf16 elements each): fp8 codes + scale,
 // bf16 copy, or bf16 quantised and dequantised (qdq).

@@ -18,7 +18,11 @@
 //   - partial dots are summed across the lanes of a slot with DPP row ops;
 //   - a chunk's scores are staged in LDS and written with 16-byte
 //     non-temporal stores: scattered 4-byte score stores interleaved with
-//     the key stream cost ~10% of the bandwidth.
+//     the key stream cost ~10% of the bandwidth;
+//   - paged caches (a block table maps each page-sized run of a sequence's
+//     slots to a page of a shared pool, pages a power of two >= 64 slots):
+//     a wave's 64 consecutive slots of one load round never straddle a page,
+//     so one table lookup per round gives their rows.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -94,10 +98,11 @@ __device__ __forceinline__ float dot8_bf16(const float* qv, u32x4 v)
 
 // bf16 keys: slot = 256 B = 16 lanes x 16 B.  Per wave and buffer:
 // kUnroll x 4 consecutive slots.
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ positions, int32_t valid_len, int32_t H, int32_t S_max, float scale,
-    float* __restrict__ scores, uint32_t* __restrict__ zero_ptr, size_t zero_words)
+    float* __restrict__ scores, uint32_t* __restrict__ zero_ptr, size_t zero_words, PageMap pm)
 {
     clear_words(zero_ptr, zero_words);
     constexpr int kUnroll = kUnrollBf16;
@@ -119,17 +124,23 @@ __global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;      // slot within a group of 4
     const int dblk = lane & 15;   // dims 8*dblk .. 8*dblk+7
-    const uint16_t* __restrict__ kr = k + (size_t)r * S_max * 128 + dblk * 8;
     constexpr int kWaveSlots = 4 * kUnroll;
     constexpr int kIterSlots = 4 * kWaveSlots;
+    // keys of the wave's slots [base, base + 64) start at row store_row(base)
+    auto round_keys = [&](const int base) {
+        return k + store_row<PAGED>(pm, r, base, S_max) * 128 + dblk * 8;
+    };
 
     u32x4 buf[kUnroll];
     int base = s0 + wave * kWaveSlots;
+    {
+        const uint16_t* __restrict__ kr = round_keys(base);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int s = base + 4 * u + g;
-        buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
-                          : u32x4{0, 0, 0, 0};
+        for (int u = 0; u < kUnroll; ++u) {
+            const int s = base + 4 * u + g;
+            buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)(4 * u + g) * 128))
+                              : u32x4{0, 0, 0, 0};
+        }
     }
 
     fold_query(q + (size_t)r * H * 128, w + (size_t)r * H, H, scale, red, qe);
@@ -143,10 +154,12 @@ __global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
         for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
         const int nb = base + kIterSlots;
         if (nb < se) {
+            const uint16_t* __restrict__ kr = round_keys(nb);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int s = nb + 4 * u + g;
-                buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
+                buf[u] = (s < se) ? __builtin_nontemporal_load(
+                                        reinterpret_cast<const u32x4*>(kr + (size_t)(4 * u + g) * 128))
                                   : u32x4{0, 0, 0, 0};
             }
         }
@@ -181,10 +194,12 @@ __device__ __forceinline__ float dot16_fp8(const float* qv, u32x4 v)
     return p;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ positions, int32_t valid_len, int32_t H,
-    int32_t S_max, float scale, float* __restrict__ scores, uint32_t* __restrict__ zero_ptr, size_t zero_words)
+    int32_t S_max, float scale, float* __restrict__ scores, uint32_t* __restrict__ zero_ptr, size_t zero_words,
+    PageMap pm)
 {
     clear_words(zero_ptr, zero_words);
     constexpr int kUnroll = kUnrollFp8;
@@ -206,24 +221,26 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 3;     // slot within a group of 8
     const int dblk = lane & 7;   // dims 16*dblk .. 16*dblk+15
-    const uint8_t* __restrict__ kr = k + (size_t)r * S_max * 128 + dblk * 16;
-    const float* __restrict__ ksr = k_scale + (size_t)r * S_max;
     constexpr int kWaveSlots = 8 * kUnroll;
     constexpr int kIterSlots = 4 * kWaveSlots;
 
+    // codes and scales of the wave's slots [base, base + 64) start at row store_row(base)
     u32x4 buf[kUnroll];
     float sbuf;
     int base = s0 + wave * kWaveSlots;
+    auto load_round = [&](const int b0) {
+        const size_t row0 = store_row<PAGED>(pm, r, b0, S_max);
+        const uint8_t* __restrict__ kr = k + row0 * 128 + dblk * 16;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const int s = base + 8 * u + g;
-        buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
-                          : u32x4{0, 0, 0, 0};
-    }
-    {
-        const int s = base + 8 * dblk + g;
-        sbuf = (s < se) ? ksr[s] : 0.f;
-    }
+        for (int u = 0; u < kUnroll; ++u) {
+            const int s = b0 + 8 * u + g;
+            buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)(8 * u + g) * 128))
+                              : u32x4{0, 0, 0, 0};
+        }
+        const int s = b0 + 8 * dblk + g;
+        sbuf = (s < se) ? k_scale[row0 + 8 * dblk + g] : 0.f;
+    };
+    load_round(base);
 
     fold_query(q + (size_t)r * H * 128, w + (size_t)r * H, H, scale, red, qe);
     float qv[16];
@@ -236,16 +253,7 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
         for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
         const float cs = sbuf;
         const int nb = base + kIterSlots;
-        if (nb < se) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int s = nb + 8 * u + g;
-                buf[u] = (s < se) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + (size_t)s * 128))
-                                  : u32x4{0, 0, 0, 0};
-            }
-            const int s = nb + 8 * dblk + g;
-            sbuf = (s < se) ? ksr[s] : 0.f;
-        }
+        if (nb < se) load_round(nb);
         float part[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) part[u] = row8_sum(dot16_fp8(qv, cur[u]));
@@ -263,17 +271,27 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
 hipError_t launch_score_decode(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
                                int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
-                               size_t zero_words, hipStream_t stream)
+                               size_t zero_words, const PageMap* paging, hipStream_t stream)
 {
     const dim3 grid((S_max + kChunk - 1) / kChunk, M);
+    const PageMap pm = paging ? *paging : PageMap{nullptr, 0, 0, 0};
+    const auto* qq = static_cast<const uint16_t*>(q);
     if (key_fp8) {
-        score_decode_fp8_kernel<<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), k_scale, positions,
-            valid_len, H, S_max, scale, scores, zero_ptr, zero_words);
+        const auto* kc = static_cast<const uint8_t*>(k_cache);
+        if (paging)
+            score_decode_fp8_kernel<true><<<grid, kThreads, 0, stream>>>(qq, w, kc, k_scale, positions, valid_len, H,
+                                                                         S_max, scale, scores, zero_ptr, zero_words, pm);
+        else
+            score_decode_fp8_kernel<false><<<grid, kThreads, 0, stream>>>(qq, w, kc, k_scale, positions, valid_len, H,
+                                                                          S_max, scale, scores, zero_ptr, zero_words, pm);
     } else {
-        score_decode_bf16_kernel<<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k_cache), positions, valid_len, H,
-            S_max, scale, scores, zero_ptr, zero_words);
+        const auto* kc = static_cast<const uint16_t*>(k_cache);
+        if (paging)
+            score_decode_bf16_kernel<true><<<grid, kThreads, 0, stream>>>(qq, w, kc, positions, valid_len, H, S_max,
+                                                                          scale, scores, zero_ptr, zero_words, pm);
+        else
+            score_decode_bf16_kernel<false><<<grid, kThreads, 0, stream>>>(qq, w, kc, positions, valid_len, H, S_max,
+                                                                           scale, scores, zero_ptr, zero_words, pm);
     }
     return hipGetLastError();
 }

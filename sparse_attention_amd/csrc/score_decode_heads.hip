@@ -35,7 +35,9 @@
 //   * scores are staged in LDS and written with 16-byte stores; chunks past
 //     n_valid only write the mask bound;
 //   * like the folded scorer, the launch can clear an unrelated buffer (the
-//     top-k workspace header of a decode step) on the side.
+//     top-k workspace header of a decode step) on the side;
+//   * paged caches: a 16-slot tile never straddles a page (pages are a power
+//     of two >= 64 slots), so one table lookup per tile gives its rows.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -80,12 +82,12 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t lo, uint32_t hi)
                  pack_bf16x2(d[0], d[1])};
 }
 
-template <bool FP8>
+template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ positions, int32_t valid_len, int32_t H,
     int32_t S_max, int32_t cpw, float scale, float* __restrict__ scores, uint32_t* __restrict__ zero_ptr,
-    size_t zero_words)
+    size_t zero_words, PageMap pm)
 {
     clear_words(zero_ptr, zero_words);
     __shared__ __attribute__((aligned(16))) float stage[kChunk * kMaxCpw];
@@ -107,15 +109,15 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
     const int g = lane >> 4;  // lane group
     const int nht = (H + 15) >> 4;
     constexpr int kSlotBytes = FP8 ? 128 : 256;
-    const uint8_t* __restrict__ kr = k + (size_t)r * S_max * kSlotBytes;
 
     // keys of tile i (slots sb .. sb + 15) as four B operands
     const int wbase = s0 + 128 * wave;
     auto tile_base = [&](const int i) { return wbase + kChunk * (i >> 3) + 16 * (i & 7); };
     auto load_tile = [&](const int i, u32x4 (&kb)[4]) {
-        const int s = tile_base(i) + n;
+        const int sb = tile_base(i);
+        const int s = sb + n;
         if (s < se) {
-            const uint8_t* p = kr + (size_t)s * kSlotBytes;
+            const uint8_t* p = k + (store_row<PAGED>(pm, r, sb, S_max) + n) * kSlotBytes;
             if (FP8) {
                 const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + 32 * g);
                 const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + 32 * g + 16);
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
 #pragma unroll
                 for (int t = 0; t < 4; ++t) kb[t] = fp8x8_to_bf16(kb[t][0], kb[t][1]);
             }
-            const float ks = FP8 ? (sb + n < se ? k_scale[(size_t)r * S_max + sb + n] : 0.f) : 1.f;
+            const float ks = FP8 ? (sb + n < se ? k_scale[store_row<PAGED>(pm, r, sb, S_max) + n] : 0.f) : 1.f;
             float acc = 0.f;
 #pragma unroll
             for (int ht = 0; ht < kMaxHeadTiles; ++ht) {
@@ -205,20 +207,27 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
 hipError_t launch_score_decode_heads(const void* q, const float* w, const void* k_cache, const float* k_scale,
                                      bool key_fp8, const int32_t* positions, int32_t valid_len, int32_t M,
                                      int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
-                                     size_t zero_words, hipStream_t stream)
+                                     size_t zero_words, const PageMap* paging, hipStream_t stream)
 {
     const int chunks = (S_max + kChunk - 1) / kChunk;
     const long long total = (long long)chunks * M;
     const int cpw = (int)std::min<long long>(kMaxCpw, std::max<long long>(1, (total + kTargetWgs - 1) / kTargetWgs));
     const dim3 grid((chunks + cpw - 1) / cpw, M);
-    if (key_fp8)
-        score_decode_heads_kernel<true><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), k_scale, positions, valid_len,
-            H, S_max, cpw, scale, scores, zero_ptr, zero_words);
-    else
-        score_decode_heads_kernel<false><<<grid, kThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(q), w, static_cast<const uint8_t*>(k_cache), nullptr, positions, valid_len,
-            H, S_max, cpw, scale, scores, zero_ptr, zero_words);
+    const PageMap pm = paging ? *paging : PageMap{nullptr, 0, 0, 0};
+    const auto* qq = static_cast<const uint16_t*>(q);
+    const auto* kc = static_cast<const uint8_t*>(k_cache);
+#define DSA_HEADS_LAUNCH(F8, PG)                                                                                  \
+    score_decode_heads_kernel<F8, PG><<<grid, kThreads, 0, stream>>>(qq, w, kc, F8 ? k_scale : nullptr, positions, \
+                                                                     valid_len, H, S_max, cpw, scale, scores,      \
+                                                                     zero_ptr, zero_words, pm)
+    if (key_fp8) {
+        if (paging) DSA_HEADS_LAUNCH(true, true);
+        else DSA_HEADS_LAUNCH(true, false);
+    } else {
+        if (paging) DSA_HEADS_LAUNCH(false, true);
+        else DSA_HEADS_LAUNCH(false, false);
+    }
+#undef DSA_HEADS_LAUNCH
     return hipGetLastError();
 }
 

@@ -36,6 +36,12 @@
 //   * the block's 32 list entries live in the lanes of every wave (lane % 32
 //     = entry): DMA row addresses come from a lane shuffle, the mask from a
 //     ballot.
+//   * paged KV (a block table maps each page of a sequence's slots to a page
+//     of a shared pool): the copies become structured buffer loads whose
+//     index is the pool row (stride = one KV row, range-checked by the
+//     hardware, no 2 GiB limit); a block's list entries are fetched three
+//     blocks ahead and their table lookups issued two blocks ahead, so the
+//     extra dependent load never stalls a copy.
 #include <algorithm>
 
 #include "device_common.h"
@@ -117,12 +123,14 @@ struct GatherIters {
 // EXACT: the shape is exactly (32 KSTEPS, 16 VT), so every loop has a fixed
 // trip count; otherwise they are upper bounds and loops are predicated.
 // With nsplit > 1 the results go to part_o / part_ml instead of out / lse.
-template <int KSTEPS, int VT, int ROWU, bool EXACT>
+// PAGED: kv is a page pool addressed through pm (kv rows of sequence b at
+// slot t: pool row page * 2^lp + t mod 2^lp).
+template <int KSTEPS, int VT, int ROWU, bool EXACT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const float* __restrict__ sink,
     const int32_t* __restrict__ idx, int32_t BS, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
     int32_t K_top, float sm_scale, int32_t nsplit, uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml)
+    uint16_t* __restrict__ part_o, float2* __restrict__ part_ml, PageMap pm)
 {
     __shared__ __attribute__((aligned(16))) u32x4 kvbuf0[GatherIters<ROWU>::units];
     __shared__ __attribute__((aligned(16))) u32x4 kvbuf1[GatherIters<ROWU>::units];
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const int blk0 = split * bps;
     const int nblk = max(0, min(nblk_all, blk0 + bps) - blk0);
     const int32_t* __restrict__ ilist = idx + (size_t)tok * K_top;
-    const uint16_t* __restrict__ kvb = kv + (size_t)b * S_kv * Dqk;
+    const uint16_t* __restrict__ kvb = PAGED ? kv : kv + (size_t)b * S_kv * Dqk;
 
     // q of this lane's head: B operand of QK^T (dims 32t + 8g .. +7)
     u32x4 qreg[KSTEPS];
@@ -199,20 +207,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     // every LDS operand read completely instead of counting them.  The
     // buffer's byte bound (S_kv * Dqk * 2, below 2 GiB) makes any stray
     // offset read zeros.
+    // Paged: a structured buffer (record = one KV row, record count = pool
+    // rows); the copies pass the pool row as the index.
     const __amdgpu_buffer_rsrc_t kv_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)((long long)S_kv * Dqk * 2), kBufferWord3);
+        PAGED ? __builtin_amdgcn_make_buffer_rsrc((void*)kvb, (short)(2 * Dqk), pm.n_pages << pm.lp, kBufferWord3)
+              : __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)((long long)S_kv * Dqk * 2), kBufferWord3);
     auto gather = [&](int rows_idx, u32x4* dst) {
         const int total = kBlock * rowu;
-        // byte offset of each entry's row (lane e and lane e + 32 hold entry
-        // e); a masked entry or padding reads row 0 (finite data, weight 0)
-        const int eoff = max(rows_idx, 0) * (2 * Dqk);
+        // byte offset of each entry's row, or its pool row when paged (lane e
+        // and lane e + 32 hold entry e); a masked entry or padding reads row 0
+        // (finite data, weight 0)
+        const int eoff = PAGED ? max(rows_idx, 0) : max(rows_idx, 0) * (2 * Dqk);
         // the row of unit u of the block; units past the last row are padding
         auto row_of = [&](const int u) { const int row = u / rowu; return row < kBlock ? row : 0; };
         auto one = [&](const int u0, const int roff) {
             const int u = u0 + lane;
             const int col = u - (u / rowu) * rowu;
             const int cs = col < dunits ? col : dunits - 1;  // pad unit: any valid address
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff + 16 * cs, 0, 0, 0);
+            if (PAGED)
+                __builtin_amdgcn_struct_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff, 16 * cs, 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff + 16 * cs, 0, 0, 0);
         };
         constexpr int kIt = GatherIters<ROWU>::value;
         constexpr int kFull = GatherIters<ROWU>::full;
@@ -242,10 +257,31 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     float l_run = 0.f;        // this lane's share of the running sum
     const float qk_scale = sm_scale * kLog2e;
 
+    // Paged: the table entry of a checked slot (an unconditional in-bounds
+    // load; a masked slot reads column 0) and the pool row it gives
+    const int32_t* __restrict__ btab = PAGED ? pm.table + (size_t)b * pm.max_pages : nullptr;
+    auto fetch_page = [&](int t) -> int { return PAGED ? btab[t >= 0 ? min(t >> pm.lp, pm.max_pages - 1) : 0] : 0; };
+    auto pool_row = [&](int t, int page) -> int {
+        return t < 0 ? -1
+                     : (int)((min((uint32_t)page, (uint32_t)(pm.n_pages - 1)) << pm.lp) | (uint32_t)(t & ((1 << pm.lp) - 1)));
+    };
+
     // prologue: indices of block 0 (checked) and block 1 (in flight), rows of block 0
+    // (paged: block 1 checked with its table lookup in flight, block 2 in flight)
     int cur_idx = check_idx(0, fetch_idx(0));
     int pending = fetch_idx(nblk > 1 ? 1 : 0);
-    if (nblk > 0) gather(cur_idx, kvbuf0);
+    int nxt_page = 0;
+    if (PAGED) {
+        const int page0 = fetch_page(cur_idx);
+        wait_vmem();
+        if (nblk > 0) gather(pool_row(cur_idx, page0), kvbuf0);
+        pending = check_idx(1, pending);  // block 1: checked slot ...
+        nxt_page = fetch_page(pending);   // ... and its table entry, in flight
+        // the raw entries of block 2 travel in nxt_raw
+    } else if (nblk > 0) {
+        gather(cur_idx, kvbuf0);
+    }
+    int nxt_raw = PAGED ? fetch_idx(nblk > 2 ? 2 : 0) : 0;
 
     // One block: its rows are in kb (a compile-time choice of kvbuf0 / kvbuf1,
     // so the compiler can tell the DMA into the other buffer never aliases
@@ -253,10 +289,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     auto run_block = [&](const int blk, const u32x4* kb, u32x4* nb) {
         wait_vmem();      // this wave's DMA of block blk and its index prefetch have landed
         __syncthreads();  // block blk resident for all; everyone finished block blk - 1
-        const int nxt_idx = check_idx(blk + 1, pending);
-        if (blk + 1 < nblk) gather(nxt_idx, nb);
-        // consumed only after the next wait_vmem, so its latency hides behind this block
-        pending = fetch_idx(blk + 2 < nblk ? blk + 2 : blk);
+        int nxt_idx;
+        if (PAGED) {
+            // pending: block blk + 1's checked slots, nxt_page: their table entries,
+            // nxt_raw: block blk + 2's raw entries (all landed)
+            nxt_idx = pending;
+            if (blk + 1 < nblk) gather(pool_row(nxt_idx, nxt_page), nb);
+            pending = check_idx(blk + 2, nxt_raw);
+            nxt_page = fetch_page(pending);
+            nxt_raw = fetch_idx(blk + 3 < nblk ? blk + 3 : blk);
+        } else {
+            nxt_idx = check_idx(blk + 1, pending);
+            if (blk + 1 < nblk) gather(nxt_idx, nb);
+            // consumed only after the next wait_vmem, so its latency hides behind this block
+            pending = fetch_idx(blk + 2 < nblk ? blk + 2 : blk);
+        }
         const uint64_t valid = __ballot(cur_idx >= 0);
         cur_idx = nxt_idx;
 
@@ -519,10 +566,10 @@ int splits_for(int32_t BS, int32_t Hq, int32_t K_top)
     return std::max(ns, 1);
 }
 
-template <int KSTEPS, int VT, int ROWU, bool EXACT>
+template <int KSTEPS, int VT, int ROWU, bool EXACT, bool PAGED>
 hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink, const int32_t* idx, int32_t B,
                           int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale,
-                          void* out, float* lse, void* workspace, hipStream_t stream)
+                          void* out, float* lse, void* workspace, const PageMap& pm, hipStream_t stream)
 {
     const int BS = B * S;
     const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
@@ -536,9 +583,9 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
     }
     const long long tok_per_xcd = (BS + kXcds - 1) / kXcds;
     const long long grid = tok_per_xcd * HG * ns * kXcds;
-    sparse_attn_kernel<KSTEPS, VT, ROWU, EXACT><<<(unsigned)grid, kThreads, 0, stream>>>(
+    sparse_attn_kernel<KSTEPS, VT, ROWU, EXACT, PAGED><<<(unsigned)grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), attn_sink, idx, BS, S, Hq, Dqk, Dv, S_kv,
-        K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml);
+        K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml, pm);
     if (ns > 1) {
         const long long waves = (long long)BS * Hq;
         sparse_attn_combine_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, stream>>>(
@@ -563,19 +610,21 @@ size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, i
 hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                               int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
-                              hipStream_t stream)
+                              const PageMap* paging, hipStream_t stream)
 {
     // Exact instances for the MLA decode shape (576 / 512) and the 192 / 128
     // shape; any other shape runs the predicated 576 / 512 instance.  ROWU
     // covers Dqk / 8 + ((10 - Dqk / 8) & 15) for every Dqk an instance accepts.
-    if (Dqk == 576 && Dv == 512)
-        return launch_variant<18, 32, 74, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                                lse, workspace, stream);
-    if (Dqk == 192 && Dv == 128)
-        return launch_variant<6, 8, 26, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                              lse, workspace, stream);
-    return launch_variant<18, 32, 74, false>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out,
-                                             lse, workspace, stream);
+    const PageMap pm = paging ? *paging : PageMap{nullptr, 0, 0, 0};
+#define DSA_ATTN_VARIANT(KS, VT_, RU, EX)                                                                          \
+    return paging ? launch_variant<KS, VT_, RU, EX, true>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top,    \
+                                                          sm_scale, out, lse, workspace, pm, stream)                \
+                  : launch_variant<KS, VT_, RU, EX, false>(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top,   \
+                                                           sm_scale, out, lse, workspace, pm, stream)
+    if (Dqk == 576 && Dv == 512) DSA_ATTN_VARIANT(18, 32, 74, true);
+    if (Dqk == 192 && Dv == 128) DSA_ATTN_VARIANT(6, 8, 26, true);
+    DSA_ATTN_VARIANT(18, 32, 74, false);
+#undef DSA_ATTN_VARIANT
 }
 
 }  // namespace dsa

@@ -10,7 +10,9 @@ can be regenerated on its own.
 from .gen import (  # noqa: F401
     causal_index_lists,
     normal,
+    page_table,
     quantize_fp8_blocks,
+    scatter_pages,
     uniform_int,
 )
 from .workloads import WORKLOADS, make_workload  # noqa: F401

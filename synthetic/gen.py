@@ -94,6 +94,29 @@ def causal_index_lists(seed: int, tensor_id: int, S: int, k: int, *, rows=None) 
     return torch.from_numpy(out)
 
 
+def page_table(seed: int, tensor_id: int, n_seq: int, max_pages: int, n_pages: int) -> torch.Tensor:
+    """Block table of a paged cache: every (sequence, page-of-slots) pair gets a distinct pool page,
+    drawn as a random permutation of the n_pages pool pages (n_pages >= n_seq * max_pages; the rest stay
+    unused).  int32 [n_seq, max_pages]."""
+    assert n_pages >= n_seq * max_pages
+    perm = _stream(seed, tensor_id, 0).permutation(n_pages)[: n_seq * max_pages]
+    return torch.from_numpy(perm.astype(np.int32).reshape(n_seq, max_pages))
+
+
+def scatter_pages(x: torch.Tensor, table: torch.Tensor, page_size: int, n_pages: int, fill: torch.Tensor):
+    """Storage layout only: the pool [n_pages * page_size, ...] holding x [n_seq, n_slots, ...] page by
+    page at the pages the table names; rows no slot maps to are taken from `fill` (same shape as the pool),
+    so a read through a wrong page returns unrelated data."""
+    n_seq, n_slots = x.shape[0], x.shape[1]
+    pool = fill.clone()
+    pv = pool.view((n_pages, page_size) + tuple(x.shape[2:]))
+    for r in range(n_seq):
+        for p in range((n_slots + page_size - 1) // page_size):
+            lo, hi = p * page_size, min(n_slots, (p + 1) * page_size)
+            pv[int(table[r, p]), : hi - lo] = x[r, lo:hi]
+    return pool
+
+
 def quantize_fp8_blocks(x: torch.Tensor):
     """Store x [..., D] as OCP FP8 E4M3 codes with one fp32 scale per last-axis block.
 

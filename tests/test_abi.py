@@ -149,12 +149,69 @@ def test_decode_step_validation(lib):
     a.index_flags = 0
     a.struct_size = 8
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED
-    # a struct without index_flags (the field is the last one) is still accepted: flags read as 0
-    old = ctypes.sizeof(m._DecodeArgs) - 8  # 4-byte field plus tail padding
-    assert old == m._DecodeArgs.index_flags.offset
+    # a struct without index_flags is still accepted: flags read as 0, paging as NULL
+    old = m._DecodeArgs.index_flags.offset
     a.struct_size = old
+    a.index_flags = 2                      # beyond the given size: ignored
+    a.paging = 8                           # (would be an invalid pointer)
     a.window = -1
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE  # validation went on past the size
+    a.window = 128
+    assert lib.dsa_decode_step_workspace_size(ctypes.byref(a)) == ws
+    a.window = -1
+    # a struct that ends after index_flags but before paging: paging reads as NULL
+    a.index_flags = 0
+    a.struct_size = m._DecodeArgs.paging.offset
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE
+    # paged: the descriptor is validated
+    a.struct_size = ctypes.sizeof(m._DecodeArgs)
+    a.window = 128
+    pg = m._PagedCache(A, 64, 64, 1000)  # 64 pages of 64 slots = 4096 = S_max
+    a.paging = ctypes.addressof(pg)
+    assert lib.dsa_decode_step(ctypes.byref(a), None, 0, None) == ERR_WORKSPACE  # valid up to the workspace
+    pg.max_pages = 63
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_SHAPE  # 63 * 64 < S_max
+    pg.max_pages, pg.page_size = 64, 96
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_UNSUPPORTED  # not a power of two
+    pg.page_size, pg.block_table = 64, None
+    assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_NULL
+
+
+def test_paged_validation(lib):
+    import sparse_attention_amd as m
+
+    pg = m._PagedCache(A, 8, 512, 100)
+    P = ctypes.byref(pg)
+    f = lib.dsa_index_score_paged
+
+    def score(paging=P, **kw):
+        a = dict(dict(ks=None, kd=0, M=2, H=4, D=128, S=4096, flags=0), **kw)
+        return f(_p(A), _p(A), _p(A), a["ks"], a["kd"], paging, None, -1, a["M"], a["H"], a["D"], a["S"], 1.0,
+                 a["flags"], _p(A), None)
+
+    assert score(paging=None) == ERR_NULL
+    assert score(S=4097) == ERR_SHAPE          # beyond max_pages * page_size
+    assert score(D=64) == ERR_UNSUPPORTED
+    assert score(flags=1, H=65) == ERR_UNSUPPORTED
+    pg.page_size = 32
+    assert score(S=256) == ERR_UNSUPPORTED     # pages below 64 slots
+    pg.page_size, pg.n_pages = 512, 1 << 22
+    assert score() == ERR_SHAPE                # pool rows beyond 2^31
+    pg.n_pages, pg.max_pages = 100, 0
+    assert score() == ERR_SHAPE
+    pg.max_pages = 8
+    g = lib.dsa_sparse_attn_paged
+
+    def attn(paging=P, **kw):
+        a = dict(dict(B=2, S=1, Hq=16, Dqk=576, Dv=512, S_kv=4096, K=64), **kw)
+        return g(_p(A), _p(A), None, _p(A), paging, a["B"], a["S"], a["Hq"], a["Dqk"], a["Dv"], a["S_kv"], a["K"],
+                 0.1, _p(A), None, _p(A), 1 << 30, None)
+
+    assert attn(paging=None) == ERR_NULL
+    assert attn(S_kv=4097) == ERR_SHAPE
+    assert attn(Dqk=100) == ERR_UNSUPPORTED
+    pg.block_table = A + 4
+    assert attn() == ERR_ALIGN
 
 
 def test_cache_write_validation(lib):

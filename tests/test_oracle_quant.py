@@ -150,3 +150,4 @@ def test_cache_write_placement():
     for (c, p), t in placed.items():
         assert np.array_equal(plain[c, p], kbits[t]) and np.array_equal(qdq[c, p], deq[t])
     assert np.all(plain[1, 0] == 0) and np.all(qdq[0, 1] == 0)
+
