@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--indexer-relu", action="store_true",
                     help="indexer activation max(0, .) per head (per-head MFMA scorer) instead of the identity")
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE",
+                    help="decode workloads: keep the key and KV caches in page pools of PAGE slots per page "
+                         "(a seeded random page order), read through a block table")
     ap.add_argument("--cpu-sample", type=int, default=64, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat oracle passes over the sample until this much time has been spent")
@@ -118,17 +121,47 @@ def main():
     k = w.index_topk
     K_top = k + w.window
 
+    paging = None
+    pkw = {}
+    if args.paged:
+        # page pools in a seeded random page order; the contiguous copies are dropped
+        P = args.paged
+        max_pages = (S_max + P - 1) // P
+        n_pages = B * max_pages
+        table = synthetic.page_table(w.seed, 99, B, max_pages, n_pages)
+        dst = table.flatten().long().to(dev)
+
+        def to_pool(x):
+            if x is None:
+                return None
+            pad = max_pages * P - S_max
+            if pad:
+                x = torch.nn.functional.pad(x.view(B, S_max, -1), (0, 0, 0, pad)).view((B, max_pages * P) +
+                                                                                     tuple(x.shape[2:]))
+            pool = torch.empty((n_pages * P,) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+            pool.view((n_pages, P) + tuple(x.shape[2:]))[dst] = x.reshape((B * max_pages, P) + tuple(x.shape[2:]))
+            return pool
+
+        gk, gks = to_pool(gk), to_pool(gks)
+        if has_attn:
+            gkv = to_pool(gkv)
+        torch.cuda.synchronize()
+        paging = dsa.Paging(table.to(dev), P, n_pages)
+        pkw = {"paging": paging}
+        log("page pools: %d pages of %d slots" % (n_pages, P))
     if has_attn:
         step = dsa.DecodeStep(gq, gw, gk, k_scale=gks, positions=gpos, valid_len=w.valid_len,
                               index_scale=w.index_scale, index_topk=k, window=w.window, q=gaq, kv=gkv,
-                              attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv, relu=args.indexer_relu)
+                              attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv, relu=args.indexer_relu,
+                              s_max=S_max if paging else None, **pkw)
         run_step = step
     else:
         scores_buf = torch.empty((B, S_max), dtype=torch.float32, device=dev)
 
         def run_step():
             dsa.dsa_index_score(gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos,
-                                valid_len=w.valid_len, relu=args.indexer_relu, out=scores_buf)
+                                valid_len=w.valid_len, relu=args.indexer_relu, out=scores_buf,
+                                s_max=S_max if paging else None, **pkw)
             return dsa.dsa_topk(scores_buf, k, positions=gpos, valid_len=w.valid_len)
 
     for _ in range(args.warmup):
@@ -144,7 +177,7 @@ def main():
     kern = {}
     ms_score = event_time_ms(torch, lambda: dsa.dsa_index_score(
         gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos, valid_len=w.valid_len,
-        relu=args.indexer_relu, out=scores_t), args.steps)
+        relu=args.indexer_relu, out=scores_t, s_max=S_max if paging else None, **pkw), args.steps)
     score_name = "score_decode_relu" if args.indexer_relu else "score_decode"
     kern[score_name] = {"us": ms_score * 1e3, "bytes": score_bytes,
                             "GB/s": score_bytes / ms_score / 1e6,
@@ -162,7 +195,8 @@ def main():
         attn_bytes = n_entries * Dqk * 2 + B * Hq * Dqk * 2 + B * Hq * Dv * 2 + B * K_top * 4
         attn_flops = 2.0 * Hq * n_entries * (Dqk + Dv)
         ms_attn = event_time_ms(torch, lambda: dsa.dsa_sparse_attn(gaq, gkv, gsink, lst, sm_scale=w.sm_scale,
-                                                                  dv=Dv), args.steps)
+                                                                  dv=Dv, s_kv=S_max if paging else None, **pkw),
+                                args.steps)
         kern["sparse_attn"] = {"us": ms_attn * 1e3, "bytes": attn_bytes, "flops": attn_flops,
                                "GB/s": attn_bytes / ms_attn / 1e6,
                                "hbm_frac": attn_bytes / ms_attn / 1e6 / HBM_PEAK_GBS,
@@ -190,7 +224,7 @@ def main():
         with open(PMC_FILE) as f:
             pmc = json.load(f)
         if pmc.get("kernel") == dom and pmc.get("source_sha") == kernel_source_sha(dom) and \
-                pmc.get("workload") == args.workload:
+                pmc.get("workload") == args.workload and not args.paged and not args.indexer_relu:
             traffic = pmc.get("hbm_bytes_per_launch")
     if dom == "sparse_attn":
         roof = {"bound": "mfma", "achieved": attn_flops / ms_attn / 1e9, "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -224,6 +258,7 @@ def main():
                    "index_heads": H, "head_dim": D, "key_dtype": "fp8_e4m3" if w.key_fp8 else "bf16",
                    "index_topk": k, "window": w.window,
                    "indexer_activation": "relu" if args.indexer_relu else "identity",
+                   "kv_layout": ("paged, %d-slot pages" % args.paged) if args.paged else "contiguous",
                    **({"attn_heads": int(w.q.shape[2]), "dqk": int(w.q.shape[3]), "dv": w.dv} if has_attn else {}),
                    "parallelism": "single-gpu"},
         "decode_tokens_per_s": B / ms_step * 1e3,

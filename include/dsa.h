@@ -266,7 +266,7 @@ dsa_status_t dsa_index_score_paged(const void* q, const float* w, const void* k_
 
 /* dsa_sparse_attn over a paged KV pool: topk_idx holds logical slots of
  * each sequence (masked unless 0 <= slot < S_kv), looked up through the
- * block table; the pool itself has no 2 GiB limit.  Workspace as for
+ * block table; the pool has no size limit beyond the page limits below.  Workspace as for
  * dsa_sparse_attn (same size query). */
 dsa_status_t dsa_sparse_attn_paged(const void* q, const void* kv_pool, const float* attn_sink,
                                    const int32_t* topk_idx, const dsa_paged_cache_t* paging, int32_t B, int32_t S,

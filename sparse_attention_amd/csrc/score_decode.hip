@@ -126,13 +126,16 @@ __global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
     const int dblk = lane & 15;   // dims 8*dblk .. 8*dblk+7
     constexpr int kWaveSlots = 4 * kUnroll;
     constexpr int kIterSlots = 4 * kWaveSlots;
-    // keys of the wave's slots [base, base + 64) start at row store_row(base)
+    // keys of the wave's slots [base, base + 64) start at row store_row(base).
+    // Paged, the rows of the next round are looked up one round ahead (the
+    // table read is a dependent load in front of that round's key loads).
     auto round_keys = [&](const int base) {
         return k + store_row<PAGED>(pm, r, base, S_max) * 128 + dblk * 8;
     };
 
     u32x4 buf[kUnroll];
     int base = s0 + wave * kWaveSlots;
+    const uint16_t* __restrict__ kr_next = round_keys(base + kIterSlots);
     {
         const uint16_t* __restrict__ kr = round_keys(base);
 #pragma unroll
@@ -154,7 +157,8 @@ __global__ __launch_bounds__(kThreads) void score_decode_bf16_kernel(
         for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
         const int nb = base + kIterSlots;
         if (nb < se) {
-            const uint16_t* __restrict__ kr = round_keys(nb);
+            const uint16_t* __restrict__ kr = kr_next;
+            kr_next = round_keys(nb + kIterSlots);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int s = nb + 4 * u + g;
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
     u32x4 buf[kUnroll];
     float sbuf;
     int base = s0 + wave * kWaveSlots;
-    auto load_round = [&](const int b0) {
-        const size_t row0 = store_row<PAGED>(pm, r, b0, S_max);
+    size_t row_next = store_row<PAGED>(pm, r, base + kIterSlots, S_max);  // next round's rows, looked up ahead
+    auto load_round = [&](const int b0, const size_t row0) {
         const uint8_t* __restrict__ kr = k + row0 * 128 + dblk * 16;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
         const int s = b0 + 8 * dblk + g;
         sbuf = (s < se) ? k_scale[row0 + 8 * dblk + g] : 0.f;
     };
-    load_round(base);
+    load_round(base, store_row<PAGED>(pm, r, base, S_max));
 
     fold_query(q + (size_t)r * H * 128, w + (size_t)r * H, H, scale, red, qe);
     float qv[16];
@@ -253,7 +257,11 @@ __global__ __launch_bounds__(kThreads) void score_decode_fp8_kernel(
         for (int u = 0; u < kUnroll; ++u) cur[u] = buf[u];
         const float cs = sbuf;
         const int nb = base + kIterSlots;
-        if (nb < se) load_round(nb);
+        if (nb < se) {
+            const size_t row0 = row_next;
+            row_next = store_row<PAGED>(pm, r, nb + kIterSlots, S_max);
+            load_round(nb, row0);
+        }
         float part[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) part[u] = row8_sum(dot16_fp8(qv, cur[u]));

@@ -37,11 +37,14 @@
 //     = entry): DMA row addresses come from a lane shuffle, the mask from a
 //     ballot.
 //   * paged KV (a block table maps each page of a sequence's slots to a page
-//     of a shared pool): the copies become structured buffer loads whose
-//     index is the pool row (stride = one KV row, range-checked by the
-//     hardware, no 2 GiB limit); a block's list entries are fetched three
-//     blocks ahead and their table lookups issued two blocks ahead, so the
-//     extra dependent load never stalls a copy.
+//     of a shared pool): a pool may exceed 4 GiB, which one buffer
+//     descriptor cannot span (buffer offsets, also of structured buffers,
+//     are 32-bit), so the paged copies are global LDS loads with per-lane
+//     64-bit addresses; a block's list entries are fetched three blocks
+//     ahead and their table lookups issued two blocks ahead, so the extra
+//     dependent load never stalls a copy.  The compiler waits for all LDS
+//     reads around such copies (lgkmcnt(0)), which costs the paged instance
+//     about 14% against the buffer-load copies of the contiguous one.
 #include <algorithm>
 
 #include "device_common.h"
@@ -207,11 +210,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     // every LDS operand read completely instead of counting them.  The
     // buffer's byte bound (S_kv * Dqk * 2, below 2 GiB) makes any stray
     // offset read zeros.
-    // Paged: a structured buffer (record = one KV row, record count = pool
-    // rows); the copies pass the pool row as the index.
+    // (paged copies address the pool directly, see the header)
     const __amdgpu_buffer_rsrc_t kv_rsrc =
-        PAGED ? __builtin_amdgcn_make_buffer_rsrc((void*)kvb, (short)(2 * Dqk), pm.n_pages << pm.lp, kBufferWord3)
-              : __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, (int)((long long)S_kv * Dqk * 2), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)kvb, 0, PAGED ? 0 : (int)((long long)S_kv * Dqk * 2), kBufferWord3);
     auto gather = [&](int rows_idx, u32x4* dst) {
         const int total = kBlock * rowu;
         // byte offset of each entry's row, or its pool row when paged (lane e
@@ -225,7 +226,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
             const int col = u - (u / rowu) * rowu;
             const int cs = col < dunits ? col : dunits - 1;  // pad unit: any valid address
             if (PAGED)
-                __builtin_amdgcn_struct_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff, 16 * cs, 0, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(reinterpret_cast<const char*>(kvb) + (size_t)(uint32_t)roff * (2 * Dqk) + 16 * cs),
+                    (lds_void*)(dst + u0), 16, 0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(kv_rsrc, (lds_void*)(dst + u0), 16, roff + 16 * cs, 0, 0, 0);
         };

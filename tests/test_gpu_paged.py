@@ -103,11 +103,12 @@ def test_paged_attn(dsa, P):
     assert torch.equal(out, flat) and torch.equal(lse, flat_lse)
 
 
-def test_paged_attn_pool_beyond_2gib(dsa):
-    """The sequences' pages sit at the far end of a 2.4 GB KV pool (rows past 2^31 bytes)."""
+def test_paged_attn_pool_beyond_4gib(dsa):
+    """The sequences' pages sit at the far end of a 4.8 GB KV pool (rows past 2^32 bytes, beyond what
+    one 32-bit buffer offset reaches)."""
     B, S_kv, Hq, Dqk, Dv, K_top, P = 2, 4096, 64, 576, 512, 512, 64
     max_pages = S_kv // P
-    n_pages = (1 << 21) // P  # 2^21 rows x 1152 B = 2.4 GB
+    n_pages = (1 << 22) // P  # 2^22 rows x 1152 B = 4.8 GB
     announce("dsa_sparse_attn_paged pool of %d rows (%.1f GB), pages at its end" % (n_pages * P,
                                                                                    n_pages * P * Dqk * 2 / 1e9))
     q = synthetic.normal(80, 0, (B, 1, Hq, Dqk))
@@ -115,9 +116,9 @@ def test_paged_attn_pool_beyond_2gib(dsa):
     sink = synthetic.normal(82, 0, (Hq,), dtype=torch.float32)
     g = np.random.default_rng(83)
     idx = torch.from_numpy(g.integers(0, S_kv, size=(B, 1, K_top)).astype(np.int32))
-    # pages n_pages - 1, n_pages - 2, ... (reversed), all beyond the 2 GiB mark
+    # pages n_pages - 1, n_pages - 2, ... (reversed), all beyond the 4 GiB mark
     table = torch.arange(n_pages - 1, n_pages - 1 - B * max_pages, -1, dtype=torch.int32).view(B, max_pages)
-    assert int(table.min()) * P * Dqk * 2 > (1 << 31)
+    assert int(table.min()) * P * Dqk * 2 > (1 << 32)
     pool = torch.zeros((n_pages * P, Dqk), dtype=torch.bfloat16, device="cuda")
     pool.view(n_pages, P, Dqk)[table.flatten().long().cuda()] = kv.cuda().view(B * max_pages, P, Dqk)
     paging = dsa.Paging(_cuda(table), P, n_pages)
