@@ -9,9 +9,9 @@
  *                     with the always-selected sliding window
  *   dsa_cache_write   new keys stored in the key cache at their positions,
  *                     optionally FP8 block-quantised
- *   dsa_index_score_paged, dsa_sparse_attn_paged
- *                     the decode scorer and the attention over paged caches
- *                     (a block table into a shared page pool)
+ *   dsa_index_score_paged, dsa_sparse_attn_paged, dsa_cache_write_paged
+ *                     the decode scorer, the attention and the key write
+ *                     over paged caches (a block table into a page pool)
  *
  * Sources (web pages, cited by title and section):
  *   [NKI-V32]   AWS Neuron "DeepSeek-V3.2 Sparse Indexer Kernel API Reference"
@@ -312,6 +312,16 @@ dsa_status_t dsa_sparse_attn_paged(const void* q, const void* kv_pool, const flo
 dsa_status_t dsa_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
                              const int32_t* positions, dsa_key_dtype_t k_dtype, void* k_cache, float* k_scale,
                              int32_t S_max, uint32_t flags, hipStream_t stream);
+
+/* dsa_cache_write into paged caches (see dsa_paged_cache_t): token t's key
+ * goes to pool row block_table[c][p / page_size] * page_size + p % page_size
+ * of k_pool (and its scale to the same row of k_scale_pool), c = t /
+ * rows_per_seq, p = positions[t]; positions outside [0, S_max) are skipped;
+ * S_max (the logical slot count) at most max_pages * page_size. */
+dsa_status_t dsa_cache_write_paged(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
+                                   const int32_t* positions, dsa_key_dtype_t k_dtype, void* k_pool,
+                                   float* k_scale_pool, const dsa_paged_cache_t* paging, int32_t S_max,
+                                   uint32_t flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

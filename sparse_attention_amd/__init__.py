@@ -104,6 +104,8 @@ def load_library(path: Optional[str] = None):
     lib.dsa_sparse_attn_paged.restype = st
     lib.dsa_sparse_attn_paged.argtypes = [vp, vp, vp, vp, pp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz,
                                           vp]
+    lib.dsa_cache_write_paged.restype = st
+    lib.dsa_cache_write_paged.argtypes = [vp, i32, i32, i32, vp, st, vp, vp, pp, i32, u32, vp]
     lib.dsa_cache_write.restype = st
     lib.dsa_cache_write.argtypes = [vp, i32, i32, i32, vp, st, vp, vp, i32, u32, vp]
     if path is None:
@@ -314,11 +316,12 @@ def dsa_decode_step(index_q, index_w, k_cache, **kw):
 
 
 def dsa_cache_write(k_new, positions, k_cache, *, k_scale=None, rows_per_seq: int = 1, round_scale: bool = False,
-                    qdq: bool = False) -> None:
+                    qdq: bool = False, paging: Optional[Paging] = None, s_max: Optional[int] = None) -> None:
     """Store k_new [T, 128] bf16 into k_cache [T // rows_per_seq, S_max, 128] in place at positions [T] int32.
 
     An fp8 cache (uint8 / float8_e4m3fn codes, with k_scale [n_seq, S_max] fp32) is written block-quantised;
-    a bf16 cache gets the key as is, or quantised and dequantised with ``qdq``."""
+    a bf16 cache gets the key as is, or quantised and dequantised with ``qdq``.  With ``paging``, k_cache /
+    k_scale are page pools [n_pages * page_size, ...] and ``s_max`` the logical slot count."""
     _dev(k_new, "k_new", (torch.bfloat16,))
     _dev(positions, "positions", (torch.int32,))
     _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -326,12 +329,22 @@ def dsa_cache_write(k_new, positions, k_cache, *, k_scale=None, rows_per_seq: in
     if kd == DSA_KEY_FP8_E4M3 and k_scale is None:
         raise ValueError("an fp8 key cache needs k_scale")
     T, D = k_new.shape
+    flags = (DSA_CACHE_ROUND_SCALE if round_scale else 0) | (DSA_CACHE_QDQ if qdq else 0)
+    if positions.shape != (T,) or k_cache.shape[-1] != D:
+        raise ValueError("shapes: k_new [T, D], positions [T], cache rows of D elements")
+    if paging is not None:
+        if s_max is None:
+            raise ValueError("a paged cache write needs s_max")
+        st = load_library().dsa_cache_write_paged(_ptr(k_new), T, int(rows_per_seq), D, _ptr(positions), kd,
+                                                  _ptr(k_cache), _ptr(k_scale), ctypes.byref(paging.struct),
+                                                  int(s_max), flags, _stream())
+        _check("dsa_cache_write_paged", st)
+        return
     n_seq, S_max = k_cache.shape[0], k_cache.shape[1]
-    if positions.shape != (T,) or k_cache.shape[2] != D or (T and n_seq * int(rows_per_seq) != T):
-        raise ValueError("shapes: k_new [T, D], positions [T], k_cache [T // rows_per_seq, S_max, D]")
+    if T and n_seq * int(rows_per_seq) != T:
+        raise ValueError("k_cache must be [T // rows_per_seq, S_max, D]")
     if k_scale is not None and tuple(k_scale.shape) != (n_seq, S_max):
         raise ValueError("k_scale must be [n_seq, S_max]")
-    flags = (DSA_CACHE_ROUND_SCALE if round_scale else 0) | (DSA_CACHE_QDQ if qdq else 0)
     st = load_library().dsa_cache_write(_ptr(k_new), T, int(rows_per_seq), D, _ptr(positions), kd, _ptr(k_cache),
                                         _ptr(k_scale), S_max, flags, _stream())
     _check("dsa_cache_write", st)

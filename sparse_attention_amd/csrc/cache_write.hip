@@ -23,7 +23,8 @@
 //   * the amax is a DPP max over the 16-lane row;
 //   * fp8: 8 codes per lane go out as one 8-byte store (128 contiguous bytes
 //     per token) and lane 0 of the row stores the scale;
-//   * bf16: one 16-byte store per lane.
+//   * bf16: one 16-byte store per lane;
+//   * paged caches: the slot's pool row comes from the block table.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -44,14 +45,15 @@ __device__ __forceinline__ float row16_max(float x)
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// MODE 0: fp8 codes + scale; 1: bf16 copy; 2: bf16 quantised and dequantised
-template <int MODE>
+// MODE 0: fp8 codes + scale; 1: bf16 copy; 2: bf16 quantised and dequantised.
+// PAGED: k_cache / k_scale are page pools addressed through pm.
+template <int MODE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(const uint16_t* __restrict__ k_new, int32_t T,
                                                                int32_t rows_per_seq,
                                                                const int32_t* __restrict__ positions,
                                                                uint8_t* __restrict__ k_cache,
                                                                float* __restrict__ k_scale, int32_t S_max,
-                                                               bool round_scale)
+                                                               bool round_scale, PageMap pm)
 {
     const int t = blockIdx.x * kTokPerWg + (threadIdx.x >> 4);
     const int e = threadIdx.x & 15;  // elements 8 e .. 8 e + 7
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const uint16_t* _
     if (t >= T) return;
     const int p = positions[t];
     if (p < 0 || p >= S_max) return;
-    const size_t slot = (size_t)(t / rows_per_seq) * S_max + p;
+    const size_t slot = store_row<PAGED>(pm, t / rows_per_seq, p, S_max);
 
     const u32x4 v = *reinterpret_cast<const u32x4*>(k_new + (size_t)t * 128 + 8 * e);
     if (MODE == 1) {
@@ -119,21 +121,25 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const uint16_t* _
 
 hipError_t launch_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, const int32_t* positions,
                               bool key_fp8, bool qdq, bool round_scale, void* k_cache, float* k_scale,
-                              int32_t S_max, hipStream_t stream)
+                              int32_t S_max, const PageMap* paging, hipStream_t stream)
 {
     if (T == 0) return hipSuccess;
     const dim3 grid((T + kTokPerWg - 1) / kTokPerWg);
     const auto* kn = static_cast<const uint16_t*>(k_new);
     auto* kc = static_cast<uint8_t*>(k_cache);
+    const PageMap pm = paging ? *paging : PageMap{nullptr, 0, 0, 0};
+#define DSA_CW_LAUNCH(MODE, KS, RS)                                                                                \
+    (paging ? cache_write_kernel<MODE, true><<<grid, kThreads, 0, stream>>>(kn, T, rows_per_seq, positions, kc, KS, \
+                                                                            S_max, RS, pm)                         \
+            : cache_write_kernel<MODE, false><<<grid, kThreads, 0, stream>>>(kn, T, rows_per_seq, positions, kc, KS, \
+                                                                             S_max, RS, pm))
     if (key_fp8)
-        cache_write_kernel<0><<<grid, kThreads, 0, stream>>>(kn, T, rows_per_seq, positions, kc, k_scale, S_max,
-                                                             round_scale);
+        DSA_CW_LAUNCH(0, k_scale, round_scale);
     else if (qdq)
-        cache_write_kernel<2><<<grid, kThreads, 0, stream>>>(kn, T, rows_per_seq, positions, kc, nullptr, S_max,
-                                                             round_scale);
+        DSA_CW_LAUNCH(2, nullptr, round_scale);
     else
-        cache_write_kernel<1><<<grid, kThreads, 0, stream>>>(kn, T, rows_per_seq, positions, kc, nullptr, S_max,
-                                                             false);
+        DSA_CW_LAUNCH(1, nullptr, false);
+#undef DSA_CW_LAUNCH
     return hipGetLastError();
 }
 

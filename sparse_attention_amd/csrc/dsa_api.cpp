@@ -356,7 +356,23 @@ dsa_status_t dsa_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq,
     if (s != DSA_OK) return s;
     return launch_status(dsa::launch_cache_write(k_new, T, rows_per_seq, positions, k_dtype == DSA_KEY_FP8_E4M3,
                                                  (flags & DSA_CACHE_QDQ) != 0, (flags & DSA_CACHE_ROUND_SCALE) != 0,
-                                                 k_cache, k_scale, S_max, stream));
+                                                 k_cache, k_scale, S_max, nullptr, stream));
+}
+
+dsa_status_t dsa_cache_write_paged(const void* k_new, int32_t T, int32_t rows_per_seq, int32_t D,
+                                   const int32_t* positions, dsa_key_dtype_t k_dtype, void* k_pool,
+                                   float* k_scale_pool, const dsa_paged_cache_t* paging, int32_t S_max,
+                                   uint32_t flags, hipStream_t stream)
+{
+    dsa_status_t s =
+        check_cache_write(k_new, T, rows_per_seq, D, positions, k_dtype, k_pool, k_scale_pool, S_max, flags);
+    if (s != DSA_OK) return s;
+    dsa::PageMap pm;
+    s = check_paging(paging, S_max, &pm);
+    if (s != DSA_OK) return s;
+    return launch_status(dsa::launch_cache_write(k_new, T, rows_per_seq, positions, k_dtype == DSA_KEY_FP8_E4M3,
+                                                 (flags & DSA_CACHE_QDQ) != 0, (flags & DSA_CACHE_ROUND_SCALE) != 0,
+                                                 k_pool, k_scale_pool, S_max, &pm, stream));
 }
 
 }  // extern "C"

@@ -65,6 +65,6 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_s
 // bf16 copy, or bf16 quantised and dequantised (qdq).
 hipError_t launch_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, const int32_t* positions,
                               bool key_fp8, bool qdq, bool round_scale, void* k_cache, float* k_scale,
-                              int32_t S_max, hipStream_t stream);
+                              int32_t S_max, const PageMap* paging, hipStream_t stream);
 
 }  // namespace dsa

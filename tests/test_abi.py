@@ -240,3 +240,22 @@ def test_cache_write_validation(lib):
     assert call(pos=_p(A + 4)) == ERR_ALIGN
     assert call(T=0) == OK                         # nothing to write: nothing is enqueued
     assert call(T=0, k=None, pos=None) == OK       # (empty tensors may have no storage)
+
+
+def test_cache_write_paged_validation(lib):
+    import sparse_attention_amd as m
+
+    pg = m._PagedCache(A, 4, 64, 100)
+    f = lib.dsa_cache_write_paged
+
+    def call(paging=ctypes.byref(pg), **kw):
+        a = dict(dict(T=4, rps=1, D=128, kd=1, ks=_p(A), S=256, flags=0), **kw)
+        return f(_p(A), a["T"], a["rps"], a["D"], _p(A), a["kd"], _p(A), a["ks"], paging, a["S"], a["flags"], None)
+
+    assert call(paging=None) == ERR_NULL
+    assert call(S=257) == ERR_SHAPE            # beyond max_pages * page_size
+    assert call(ks=None) == ERR_NULL
+    assert call(flags=2) == ERR_UNSUPPORTED
+    pg.page_size = 48
+    assert call() == ERR_UNSUPPORTED
+

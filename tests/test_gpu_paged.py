@@ -167,3 +167,44 @@ def test_paged_decode_step(dsa, relu):
     # equal up to the summation order
     assert torch.equal(step.index_list.sort(dim=1).values, flat.index_list.sort(dim=1).values)
     check_attn(step.out.float().cpu().numpy(), flat.out.float().cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_paged_cache_write_then_score(dsa, fp8):
+    """New keys written into a paged cache (fp8: quantised), then scored through the same table: pool bytes
+    equal the oracle's cache write read back through its unpaging, and the scores match the oracle."""
+    M, S_max, P = 4, 2000, 64
+    w = synthetic.make_workload("batched_decode", M=M, H=64, S_max=S_max, pos_lo=0, topk=64)
+    w.positions = torch.tensor([5, 1999, 64, 1000], dtype=torch.int32)
+    announce("dsa_cache_write_paged fp8=%s page=%d then dsa_index_score_paged" % (fp8, P))
+    keys = synthetic.normal(95, 0, (M * S_max, 128))          # every slot's key, written in one call
+    pos_all = np.tile(np.arange(S_max, dtype=np.int32), M)
+    max_pages = -(-S_max // P)
+    n_pages = M * max_pages + 3
+    table = synthetic.page_table(96, 11, M, max_pages, n_pages)
+    paging = dsa.Paging(_cuda(table), P, n_pages)
+    if fp8:
+        pool = torch.zeros((n_pages * P, 128), dtype=torch.uint8, device="cuda")
+        spool = torch.zeros((n_pages * P,), dtype=torch.float32, device="cuda")
+    else:
+        pool = torch.zeros((n_pages * P, 128), dtype=torch.bfloat16, device="cuda")
+        spool = None
+    dsa.dsa_cache_write(keys.cuda(), torch.from_numpy(pos_all).cuda(), pool, k_scale=spool, rows_per_seq=S_max,
+                        paging=paging, s_max=S_max)
+    got = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), pool, scale=w.index_scale, k_scale=spool,
+                              positions=_cuda(w.positions), paging=paging, s_max=S_max)
+    torch.cuda.synchronize()
+    if fp8:
+        c0 = np.zeros((M, S_max, 128), np.uint8)
+        s0 = np.zeros((M, S_max), np.float32)
+        want_c, want_s = oracle.cache_write(keys, pos_all, c0, s0, rows_per_seq=S_max)
+        assert np.array_equal(oracle.unpage(pool, table, P, S_max), want_c)
+        assert np.array_equal(oracle.unpage(spool, table, P, S_max), want_s)
+        ref = oracle.index_score(w.index_q, w.index_w, want_c, k_scale=want_s, scale=w.index_scale,
+                                 positions=w.positions)
+    else:
+        want = oracle.cache_write(keys, pos_all, np.zeros((M, S_max, 128), np.uint16), rows_per_seq=S_max)
+        assert np.array_equal(oracle.unpage(pool, table, P, S_max), want)
+        ref = oracle.index_score(w.index_q, w.index_w, want, scale=w.index_scale, positions=w.positions)
+    nv = n_valid_rows(w.positions.numpy(), -1, M, S_max)
+    check_scores(got.cpu().numpy(), ref, nv, oracle.mask_bound())
