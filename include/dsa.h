@@ -113,7 +113,9 @@ float dsa_mask_bound(void);
  *
  * Limits: D == 128; 1 <= H <= 128; M >= 1; S_max >= 1; M % rows_per_seq == 0.
  * rows_per_seq == 1: M <= 65535; with DSA_SCORE_RELU also H <= 64.
- * rows_per_seq > 1 requires bf16 keys, H <= 64 and S_max * 256 bytes below 2 GiB.
+ * rows_per_seq > 1 requires bf16 keys and S_max * 256 bytes below 2 GiB, and
+ * with DSA_SCORE_RELU also H <= 64.  (With the identity activation the
+ * heads fold by linearity into one fp32 query per row, as in decode.)
  * Otherwise DSA_ERR_SHAPE / DSA_ERR_UNSUPPORTED.
  */
 dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache, const float* k_scale,

@@ -39,8 +39,8 @@ dsa_status_t check_index_score(const void* q, const float* w, const void* k_cach
         if ((flags & DSA_SCORE_RELU) && H > 64) return DSA_ERR_UNSUPPORTED;  // per-head MFMA path: 4 head tiles
         if (M > 65535) return DSA_ERR_SHAPE;
     } else {
-        if (k_dtype != DSA_KEY_BF16 || H > 64) return DSA_ERR_UNSUPPORTED;
-        if (!dsa::score_prefill_available()) return DSA_ERR_UNSUPPORTED;
+        if (k_dtype != DSA_KEY_BF16) return DSA_ERR_UNSUPPORTED;
+        if ((flags & DSA_SCORE_RELU) && (H > 64 || !dsa::score_prefill_available())) return DSA_ERR_UNSUPPORTED;
         if ((long long)S_max * D * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's keys: 32-bit offsets
     }
     if (!aligned16(q) || !aligned16(k_cache)) return DSA_ERR_ALIGN;
@@ -216,8 +216,13 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
         return launch_status(dsa::launch_score_decode(q, w, k_cache, k_scale, k_dtype == DSA_KEY_FP8_E4M3, positions,
                                                       valid_len, M, H, S_max, scale, scores, nullptr, 0, nullptr,
                                                       stream));
+    // prefill: with the identity activation the heads fold into one query per
+    // row (bound by the score writes); ReLU needs the per-head MFMA contraction
+    if (!(flags & DSA_SCORE_RELU))
+        return launch_status(dsa::launch_score_prefill_fold(q, w, k_cache, positions, valid_len, M, rows_per_seq, H,
+                                                            S_max, scale, scores, stream));
     return launch_status(dsa::launch_score_prefill(q, w, k_cache, positions, valid_len, M, rows_per_seq, H, S_max,
-                                                   scale, (flags & DSA_SCORE_RELU) != 0, scores, stream));
+                                                   scale, true, scores, stream));
 }
 
 size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk)

@@ -35,6 +35,12 @@ hipError_t launch_score_decode_heads(const void* q, const float* w, const void* 
 // Whether this build contains the prefill (per-head MFMA) scoring kernel.
 bool score_prefill_available();
 
+// Prefill indexer score with the identity activation: the heads folded into one
+// fp32 query per row (split into bf16 hi + lo MFMA operands); bf16 keys.
+hipError_t launch_score_prefill_fold(const void* q, const float* w, const void* k_cache, const int32_t* positions,
+                                     int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,
+                                     float scale, float* scores, hipStream_t stream);
+
 // Prefill indexer score: rows_per_seq query rows share one bf16 cache; per-head MFMA.
 hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cache, const int32_t* positions,
                                 int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,

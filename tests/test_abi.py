@@ -76,8 +76,8 @@ def test_index_score_validation(lib):
     assert call(flags=4) == ERR_UNSUPPORTED
     assert call(q=_p(A + 8)) == ERR_ALIGN
     assert call(kd=7) == ERR_UNSUPPORTED
-    # prefill (rows_per_seq > 1): per-head MFMA path, bf16 keys, at most 64 heads
-    assert call(M=4, rps=4, H=65) == ERR_UNSUPPORTED
+    # prefill (rows_per_seq > 1): bf16 keys; the per-head MFMA path (ReLU) takes at most 64 heads
+    assert call(M=4, rps=4, H=65, flags=1) == ERR_UNSUPPORTED
     assert call(M=4, rps=4, kd=1, ks=_p(A)) == ERR_UNSUPPORTED
 
 

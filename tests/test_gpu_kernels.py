@@ -124,8 +124,9 @@ def test_score_decode_fp8_all_codes(dsa):
     _score_case(dsa, w, "fp8 all codes")
 
 
+# identity: the folded-query kernel (any H up to 128); ReLU: the per-head MFMA kernel (H <= 64)
 @pytest.mark.parametrize("S,H,relu", [(300, 64, False), (300, 64, True), (77, 4, False), (130, 40, True),
-                                       (513, 64, False)])
+                                       (513, 64, False), (300, 128, False), (33, 1, False), (31, 64, True)])
 def test_score_prefill_causal(dsa, S, H, relu):
     w = synthetic.make_workload("prefill", S=S, H=H, topk=64)
     announce("dsa_index_score prefill S=%d H=%d relu=%s" % (S, H, relu))
