@@ -222,7 +222,7 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
         return launch_status(dsa::launch_score_prefill_fold(q, w, k_cache, positions, valid_len, M, rows_per_seq, H,
                                                             S_max, scale, scores, stream));
     return launch_status(dsa::launch_score_prefill(q, w, k_cache, positions, valid_len, M, rows_per_seq, H, S_max,
-                                                   scale, true, scores, stream));
+                                                   scale, scores, stream));
 }
 
 size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk)

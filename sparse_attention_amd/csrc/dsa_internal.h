@@ -41,10 +41,11 @@ hipError_t launch_score_prefill_fold(const void* q, const float* w, const void* 
                                      int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,
                                      float scale, float* scores, hipStream_t stream);
 
-// Prefill indexer score: rows_per_seq query rows share one bf16 cache; per-head MFMA.
+// Prefill indexer score with the per-head activation max(0, .): rows_per_seq
+// query rows share one bf16 cache; per-head MFMA, H <= 64.
 hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cache, const int32_t* positions,
                                 int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,
-                                float scale, bool relu, float* scores, hipStream_t stream);
+                                float scale, float* scores, hipStream_t stream);
 
 // Top-k per row.  With window > 0 the output row has width k + window and
 // holds the top-k with in-window entries replaced by -1, followed by the

@@ -31,9 +31,9 @@
 //     barrier so that the wait for a stage's copy does not wait on them;
 //   * stages past a group's causal limit are skipped; the mask-bound rest of
 //     each row goes out with 16-byte stores spread over the stages.
-// The identity-phi fold used for decode (one pre-summed query per row) is
-// not used here: on bf16 MFMA it would round the folded query to bf16, and
-// it does not exist for phi = ReLU.
+// This per-head form serves phi = ReLU, which does not commute with the head
+// sum.  With the identity activation the heads fold into one query per row
+// (score_prefill_fold.hip), which needs 1/H of these flops.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -319,18 +319,15 @@ bool score_prefill_available() { return true; }
 
 hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cache, const int32_t* positions,
                                 int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,
-                                float scale, bool relu, float* scores, hipStream_t stream)
+                                float scale, float* scores, hipStream_t stream)
 {
+    // the identity activation folds over heads instead (score_prefill_fold.hip)
     const int n_seq = M / rows_per_seq;
     const int groups = n_seq * ((rows_per_seq + kQ - 1) / kQ);
     auto* qp = static_cast<const uint16_t*>(q);
     auto* kp = static_cast<const uint16_t*>(k_cache);
-    if (relu)
-        score_prefill_kernel<true><<<groups, kThreads, 0, stream>>>(qp, w, kp, positions, valid_len, rows_per_seq, H,
-                                                                    S_max, scale, scores);
-    else
-        score_prefill_kernel<false><<<groups, kThreads, 0, stream>>>(qp, w, kp, positions, valid_len, rows_per_seq, H,
-                                                                     S_max, scale, scores);
+    score_prefill_kernel<true><<<groups, kThreads, 0, stream>>>(qp, w, kp, positions, valid_len, rows_per_seq, H,
+                                                                S_max, scale, scores);
     return hipGetLastError();
 }
 
