@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
 METRIC = "DSA decode: indexer key-slots/s + sparse-attn tokens/s; % of HBM peak"
 PMC_FILE = os.path.join(ROOT, "profiles", "score_decode_full_decode_step.pmc.json")
 KERNEL_SOURCES = {"score_decode": "score_decode.hip", "score_decode_relu": "score_decode_heads.hip", "topk": "topk.hip",
@@ -58,6 +59,10 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=64, help="sequences in the oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat oracle passes over the sample until this much time has been spent")
+    ap.add_argument("--rotate", type=int, default=0, metavar="R",
+                    help="indexer-only workloads: cycle over R copies of the inputs at distinct addresses "
+                         "(default: enough copies for twice the 256 MB Infinity Cache, at least 4, when one "
+                         "set is smaller than that)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (scale reference for PMC byte counters)")
     return ap.parse_args()
@@ -157,12 +162,32 @@ def main():
         run_step = step
     else:
         scores_buf = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+        # Indexer-only workloads fit in the 256 MB Infinity Cache: cycle over
+        # copies of every input and output at distinct addresses so that each
+        # timed call streams from HBM (footprint >= 2 x the cache).
+        set_bytes = sum(t.numel() * t.element_size() for t in (gq, gw, gk, gks, gpos, scores_buf) if t is not None)
+        n_rot = args.rotate if args.rotate > 0 else (
+            max(4, -(-2 * MALL_BYTES // set_bytes)) if set_bytes < 2 * MALL_BYTES else 1)
+        sets = [(gq, gw, gk, gks, gpos, scores_buf)]
+        for _ in range(n_rot - 1):
+            sets.append(tuple(None if t is None else t.clone() for t in sets[0]))
+        torch.cuda.synchronize()
+        if n_rot > 1:
+            log("rotating over %d input sets of %.1f MB (%.0f MB in all)" % (n_rot, set_bytes / 1e6,
+                                                                          n_rot * set_bytes / 1e6))
+        rot = [0]
+
+        def next_set():
+            i = rot[0]
+            rot[0] = (i + 1) % n_rot
+            return sets[i]
 
         def run_step():
-            dsa.dsa_index_score(gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos,
-                                valid_len=w.valid_len, relu=args.indexer_relu, out=scores_buf,
+            q_, w_, k_, ks_, pos_, sc_ = next_set()
+            dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, k_scale=ks_, positions=pos_,
+                                valid_len=w.valid_len, relu=args.indexer_relu, out=sc_,
                                 s_max=S_max if paging else None, **pkw)
-            return dsa.dsa_topk(scores_buf, k, positions=gpos, valid_len=w.valid_len)
+            return dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len)
 
     for _ in range(args.warmup):
         run_step()
@@ -172,19 +197,33 @@ def main():
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
     log("step %.3f ms (host wall %.3f ms/step)" % (ms_step, wall_ms))
 
-    # per-kernel timings (same inputs, same stream)
+    # per-kernel timings (same inputs, same stream; the same rotation)
     scores_t = step.scores if has_attn else scores_buf
+    if has_attn:
+        n_rot = 1
+        sets = [(gq, gw, gk, gks, gpos, scores_t)]
+        rot = [0]
+
+        def next_set():
+            return sets[0]
     kern = {}
-    ms_score = event_time_ms(torch, lambda: dsa.dsa_index_score(
-        gq, gw, gk, scale=w.index_scale, k_scale=gks, positions=gpos, valid_len=w.valid_len,
-        relu=args.indexer_relu, out=scores_t, s_max=S_max if paging else None, **pkw), args.steps)
+
+    def score_once():
+        q_, w_, k_, ks_, pos_, sc_ = next_set()
+        dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, k_scale=ks_, positions=pos_, valid_len=w.valid_len,
+                            relu=args.indexer_relu, out=sc_, s_max=S_max if paging else None, **pkw)
+
+    def topk_once():
+        q_, w_, k_, ks_, pos_, sc_ = next_set()
+        dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len)
+
+    ms_score = event_time_ms(torch, score_once, args.steps)
     score_name = "score_decode_relu" if args.indexer_relu else "score_decode"
     kern[score_name] = {"us": ms_score * 1e3, "bytes": score_bytes,
                             "GB/s": score_bytes / ms_score / 1e6,
                             "hbm_frac": score_bytes / ms_score / 1e6 / HBM_PEAK_GBS,
                             "key_slots_per_s": n_slots / ms_score * 1e3}
-    ms_topk = event_time_ms(torch, lambda: dsa.dsa_topk(scores_t, k, positions=gpos, valid_len=w.valid_len),
-                            args.steps)
+    ms_topk = event_time_ms(torch, topk_once, args.steps)
     topk_bytes = n_slots * 4 + B * k * 4
     kern["topk"] = {"us": ms_topk * 1e3, "bytes": topk_bytes, "GB/s": topk_bytes / ms_topk / 1e6}
     step_bytes = score_bytes + topk_bytes
@@ -259,6 +298,7 @@ def main():
                    "index_topk": k, "window": w.window,
                    "indexer_activation": "relu" if args.indexer_relu else "identity",
                    "kv_layout": ("paged, %d-slot pages" % args.paged) if args.paged else "contiguous",
+                   "input_sets": n_rot,
                    **({"attn_heads": int(w.q.shape[2]), "dqk": int(w.q.shape[3]), "dv": w.dv} if has_attn else {}),
                    "parallelism": "single-gpu"},
         "decode_tokens_per_s": B / ms_step * 1e3,

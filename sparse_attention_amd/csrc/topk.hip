@@ -24,6 +24,8 @@
 //                   slots above it are written out directly (one global
 //                   atomic per workgroup reserves the output range), slots
 //                   in it are appended to the row's (key, slot) list;
+//                   chunk 0 also records the row's threshold bin and the
+//                   count above it for the resolve;
 //      topk_resolve one workgroup per row runs the two remaining digits over
 //                   the candidates.  Kernel boundaries make the other
 //                   workgroups' writes visible; an in-kernel "last
@@ -47,7 +49,7 @@ constexpr int kChunk = 4096;  // slots per workgroup in the chunked path
 constexpr int kChunkThreads = 256;
 constexpr int kRowThreads = 1024;
 constexpr int kCoarse = 256;  // top 8 key bits: sign + 7 exponent bits
-constexpr int kCtrl = 4;      // per-row counters: above-count, candidate count, (2 spare)
+constexpr int kCtrl = 4;      // per-row words: above-threshold count, candidate count, threshold bin, count above it
 constexpr int kHeaderWords = kBins + kCoarse + kCtrl;  // per-row words zeroed before each call
 constexpr int kResolveCap = 8192;  // candidates resolved from LDS; more are re-read from HBM
 constexpr int kRowLdsThreads = 512;
@@ -433,6 +435,11 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
     uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
     row_threshold(gh, k, scratch, wave_tot, &sh_digit, &sh_above);
     const uint32_t d1 = (uint32_t)sh_digit;
+    uint32_t* __restrict__ ctrl = gh + kBins + kCoarse;
+    if (blockIdx.x == 0 && t == 0) {  // for the resolve (visible after this kernel)
+        ctrl[2] = d1;
+        ctrl[3] = (uint32_t)sh_above;
+    }
 
     int my_gt = 0, my_eq = 0;
 #pragma unroll
@@ -445,7 +452,6 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
     int off_gt = my_gt ? atomicAdd(&cnt_gt, my_gt) : 0;
     int off_eq = my_eq ? atomicAdd(&cnt_eq, my_eq) : 0;
     __syncthreads();
-    uint32_t* __restrict__ ctrl = gh + kBins + kCoarse;
     if (t == 0) {
         base_gt = cnt_gt ? (int)atomicAdd(&ctrl[0], (uint32_t)cnt_gt) : 0;
         base_eq = cnt_eq ? (int)atomicAdd(&ctrl[1], (uint32_t)cnt_eq) : 0;
@@ -476,7 +482,6 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     int32_t k, int32_t window, uint32_t* __restrict__ ghist, const int2* __restrict__ cand,
     int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
 {
-    __shared__ int scratch[kCoarse];
     __shared__ int hist[kBins];
     __shared__ int2 lcand[kResolveCap];
     __shared__ int wave_tot[kChunkThreads / 64];
@@ -492,11 +497,12 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
     const int t = threadIdx.x;
 
-    uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
-    row_threshold(gh, k, scratch, wave_tot, &sh_digit, &sh_above);
-    const uint32_t d1 = (uint32_t)sh_digit;
-    const int above = sh_above;
-    const int n_cand = (int)gh[d1];  // every chunk appended its keys of bucket d1
+    // the threshold bin and the count above it, as the filter's chunk 0
+    // found them; the candidate count is the filter's running total
+    const uint32_t* __restrict__ ctrl = ghist + (size_t)r * kHeaderWords + kBins + kCoarse;
+    const int n_cand = (int)ctrl[1];
+    const uint32_t d1 = ctrl[2];
+    const int above = (int)ctrl[3];
     const bool in_lds = n_cand <= kResolveCap;
     const int2* __restrict__ crow = cand + (size_t)r * S_max;
     if (in_lds)

@@ -159,10 +159,12 @@ def test_score_prefill_several_sequences_with_offset(dsa):
 # ------------------------------------------------------------------ top-k
 
 # paths: one workgroup per row with the row in LDS (S_max <= 8192, a
-# multiple of 4), rows cut into 4096-slot chunks (longer rows, fewer than
-# 1024), one workgroup per row re-reading the row otherwise
+# multiple of 4); fewer than 1024 longer rows: a chip-wide first-digit
+# histogram over 4096-slot chunks, then one select workgroup per row (up to
+# 262144 slots) or a chip-wide filter and a per-row resolve (longer rows);
+# one workgroup per row re-reading the row otherwise
 @pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (65536, 2048), (40002, 512),
-                                     (70000, 2048), (3000, 2048)])
+                                     (70000, 2048), (3000, 2048), (300000, 2048)])
 def test_topk_edges(dsa, S_max, k):
     g = np.random.default_rng(S_max * 7 + k)
     nvs = sorted({0, 1, max(0, k - 1), k, k + 1, S_max // 2, S_max - 1, S_max})
@@ -184,9 +186,10 @@ def test_topk_edges(dsa, S_max, k):
         assert np.all(np.isneginf(tsc[i][~ok]))
 
 
-@pytest.mark.parametrize("S_max", [4000, 20000])
+@pytest.mark.parametrize("S_max", [4000, 20000, 65536, 300000])
 def test_topk_all_equal_row(dsa, S_max):
-    """Every score ties: any k of them is a valid answer (row and chunked paths)."""
+    """Every score ties: any k of them is a valid answer (row and chunked paths).  From 20000 slots the
+    tied candidates exceed the select kernel's LDS list and spill to the workspace."""
     sc = np.zeros((2, S_max), np.float32)
     announce("dsa_topk all-equal rows S_max=%d" % S_max)
     idx = dsa.dsa_topk(torch.from_numpy(sc).cuda(), 1000, valid_len=S_max - 1).cpu().numpy()
