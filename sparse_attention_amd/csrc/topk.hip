@@ -317,20 +317,23 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     static_assert(kChunkThreads == kCoarse, "one thread per coarse bin");
     __shared__ int hist[kBins];
     const int r = blockIdx.y;
-    const int nv = n_valid_of(positions, valid_len, r, S_max);
     const int s0 = blockIdx.x * kChunk;
-    if (nv <= k || s0 >= nv) return;  // uniform
-    const int s1 = min(s0 + kChunk, nv);
     const float* __restrict__ row = scores + (size_t)r * S_max;
-    for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
-    __syncthreads();
+    // The chunk's scores are loaded before n_valid is known (every slot
+    // below S_max is readable), so the position lookup overlaps them.
     constexpr int kPer = kChunk / kChunkThreads;  // 16 slots per thread: loads first, then LDS atomics
+    const int sl = min(s0 + kChunk, S_max);
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int s = s0 + i * kChunkThreads + (int)threadIdx.x;
-        v[i] = s < s1 ? row[s] : 0.f;
+        v[i] = s < sl ? row[s] : 0.f;
     }
+    const int nv = n_valid_of(positions, valid_len, r, S_max);
+    if (nv <= k || s0 >= nv) return;  // uniform
+    const int s1 = min(s0 + kChunk, nv);
+    for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
         if (s0 + i * kChunkThreads + (int)threadIdx.x < s1) atomicAdd(&hist[f32_order_key(v[i]) >> 20], 1);
@@ -352,11 +355,13 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
 
 // Threshold bucket of the first digit from the row's two-level histogram:
 // the coarse bin holding the k-th largest key, then the fine bin inside it.
-__device__ void row_threshold(const uint32_t* __restrict__ gh, int k, int* scratch, int* wave_tot, int* res_digit,
-                              int* res_above)
+// `coarse` is this thread's coarse bin, gh[kBins + threadIdx.x], loaded by
+// the caller ahead of time.
+__device__ void row_threshold(const uint32_t* __restrict__ gh, uint32_t coarse, int k, int* scratch, int* wave_tot,
+                              int* res_digit, int* res_above)
 {
     // coarse: 256 bins, one per thread
-    scratch[threadIdx.x] = (int)gh[kBins + threadIdx.x];
+    scratch[threadIdx.x] = (int)coarse;
     __syncthreads();
     find_bucket<kChunkThreads>(scratch, kCoarse, k, wave_tot, res_digit, res_above);
     const int c1 = *res_digit;
@@ -390,14 +395,29 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
 
     const int r = blockIdx.y;
     const int nchunks = gridDim.x;
+    const int s0 = blockIdx.x * kChunk;
+    const float* __restrict__ row = scores + (size_t)r * S_max;
+    const int t = threadIdx.x;
+    // Loads that do not depend on n_valid go first (every slot below S_max
+    // is readable): this chunk's scores and this thread's coarse bin, so that
+    // the position lookup, the scores and the threshold lookup share one
+    // memory latency.
+    constexpr int kPer = kChunk / kChunkThreads;  // 16 slots per thread
+    const int sl = min(s0 + kChunk, S_max);
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int s = s0 + i * kChunkThreads + t;
+        v[i] = s < sl ? row[s] : 0.f;
+    }
+    uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
+    const uint32_t coarse = gh[kBins + t];  // kChunkThreads == kCoarse
+
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     const int width = k + window;
     const int wstart = nv - window;
-    const int s0 = blockIdx.x * kChunk;
-    const float* __restrict__ row = scores + (size_t)r * S_max;
     int32_t* __restrict__ orow = out_idx + (size_t)r * width;
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
-    const int t = threadIdx.x;
 
     if (blockIdx.x == 0)
         for (int i = t; i < window; i += kChunkThreads) {
@@ -419,21 +439,18 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
         return;
     }
 
-    // this chunk's keys first (their latency overlaps the threshold lookup)
     const int s1 = min(s0 + kChunk, nv);
-    constexpr int kPer = kChunk / kChunkThreads;  // 16 slots per thread
     uint32_t keys[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int s = s0 + i * kChunkThreads + t;
-        keys[i] = (s < s1) ? f32_order_key(row[s]) : 0u;
+        keys[i] = (s < s1) ? f32_order_key(v[i]) : 0u;
     }
     if (t == 0) {
         cnt_gt = 0;
         cnt_eq = 0;
     }
-    uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
-    row_threshold(gh, k, scratch, wave_tot, &sh_digit, &sh_above);
+    row_threshold(gh, coarse, k, scratch, wave_tot, &sh_digit, &sh_above);
     const uint32_t d1 = (uint32_t)sh_digit;
     uint32_t* __restrict__ ctrl = gh + kBins + kCoarse;
     if (blockIdx.x == 0 && t == 0) {  // for the resolve (visible after this kernel)
@@ -467,7 +484,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
         const uint32_t dg = keys[i] >> 20;
         if (dg > d1) {
             orow[off_gt] = emit(s, wstart);
-            if (osc) osc[off_gt] = row[s];
+            if (osc) osc[off_gt] = v[i];
             ++off_gt;
         } else if (dg == d1) {
             crow[off_eq++] = make_int2((int)keys[i], s);
@@ -488,6 +505,13 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq;
 
     const int r = blockIdx.x;
+    // the threshold bin and the count above it, as the filter's chunk 0
+    // found them, and the candidate count (the filter's running total);
+    // read together with the position
+    const uint32_t* __restrict__ ctrl = ghist + (size_t)r * kHeaderWords + kBins + kCoarse;
+    const int n_cand = (int)ctrl[1];
+    const uint32_t d1 = ctrl[2];
+    const int above = (int)ctrl[3];
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     if (nv <= k) return;  // uniform
     const int width = k + window;
@@ -497,12 +521,6 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
     const int t = threadIdx.x;
 
-    // the threshold bin and the count above it, as the filter's chunk 0
-    // found them; the candidate count is the filter's running total
-    const uint32_t* __restrict__ ctrl = ghist + (size_t)r * kHeaderWords + kBins + kCoarse;
-    const int n_cand = (int)ctrl[1];
-    const uint32_t d1 = ctrl[2];
-    const int above = (int)ctrl[3];
     const bool in_lds = n_cand <= kResolveCap;
     const int2* __restrict__ crow = cand + (size_t)r * S_max;
     if (in_lds)
