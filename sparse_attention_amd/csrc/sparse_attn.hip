@@ -487,16 +487,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 }
 
 // Merge the nsplit partial results of every (token, head): one wave per
-// (token, head), each lane handles 8 consecutive output features.
+// (token, head), each lane handles 8 consecutive output features.  Tokens
+// are placed on the XCDs as in the main kernel (XCD x takes the x-th run of
+// ceil(BS / kXcds) tokens), so a token's partial results are read back from
+// the L2 that wrote them.
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, const float* __restrict__ sink,
     int32_t BS, int32_t Hq, int32_t Dv, int32_t nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
 {
-    const int wid = (int)(blockIdx.x * 4 + (threadIdx.x >> 6));
-    if (wid >= BS * Hq) return;  // uniform over the wave
+    const int tok_per_xcd = (BS + kXcds - 1) / kXcds;
+    const int lw = (int)((blockIdx.x / kXcds) * 4 + (threadIdx.x >> 6));  // wave within the XCD's tokens
+    const int tok = (int)(blockIdx.x % kXcds) * tok_per_xcd + lw / Hq;
+    if (lw >= tok_per_xcd * Hq || tok >= BS) return;  // uniform over the wave
     const int lane = threadIdx.x & 63;
-    const int tok = wid / Hq;
-    const int head = wid - tok * Hq;
+    const int head = lw % Hq;
     // every load in flight at once: the (max, sum) pairs and this lane's
     // first 8 output dims of every split (a split without entries holds
     // zeros and gets weight 0)
@@ -590,8 +594,8 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), attn_sink, idx, BS, S, Hq, Dqk, Dv, S_kv,
         K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml, pm);
     if (ns > 1) {
-        const long long waves = (long long)BS * Hq;
-        sparse_attn_combine_kernel<<<(unsigned)((waves + 3) / 4), 256, 0, stream>>>(
+        const long long waves_per_xcd = tok_per_xcd * Hq;
+        sparse_attn_combine_kernel<<<(unsigned)((waves_per_xcd + 3) / 4 * kXcds), 256, 0, stream>>>(
             part_o, part_ml, attn_sink, BS, Hq, Dv, ns, static_cast<uint16_t*>(out), lse);
     }
     return hipGetLastError();
