@@ -186,6 +186,27 @@ def test_topk_edges(dsa, S_max, k):
         assert np.all(np.isneginf(tsc[i][~ok]))
 
 
+@pytest.mark.parametrize("M,S_max,k", [(1100, 9001, 1024), (5, 4001, 300), (1030, 10000, 2048)])
+def test_topk_row_reread_path(dsa, M, S_max, k):
+    """The row path that re-reads each row per digit: 1024 or more rows longer than 8192 slots, or a row
+    length that is not a multiple of 4."""
+    g = np.random.default_rng(M + S_max + k)
+    sc = g.standard_normal((M, S_max)).astype(np.float32)
+    sc[::3] = np.round(sc[::3] * 8) / 8  # exact ties on every third row
+    nv = g.integers(0, S_max + 1, M)
+    nv[:4] = [0, 1, k, S_max]
+    pos = (nv - 1).astype(np.int32)
+    announce("dsa_topk row path M=%d S_max=%d k=%d" % (M, S_max, k))
+    idx, tsc = dsa.dsa_topk(torch.from_numpy(sc).cuda(), k, positions=torch.from_numpy(pos).cuda(), with_scores=True)
+    torch.cuda.synchronize()
+    idx, tsc = idx.cpu().numpy(), tsc.cpu().numpy()
+    check_topk_same_scores(idx, sc, nv, k)
+    for i in range(0, M, 97):
+        ok = idx[i] >= 0
+        assert np.array_equal(tsc[i][ok], sc[i, idx[i][ok]])
+        assert np.all(np.isneginf(tsc[i][~ok]))
+
+
 @pytest.mark.parametrize("S_max", [4000, 20000, 65536, 300000])
 def test_topk_all_equal_row(dsa, S_max):
     """Every score ties: any k of them is a valid answer (row and chunked paths).  From 20000 slots the
