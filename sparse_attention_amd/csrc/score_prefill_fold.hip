@@ -29,7 +29,11 @@
 //     operands come straight from memory (a sequence's keys stay in L2),
 //     one tile ahead;
 //   * a row tile whose rows are all past their causal limit in a key tile
-//     skips its MFMAs and only writes the mask bound.
+//     skips its MFMAs and only writes the mask bound;
+//   * q (read once) and the score matrix (written once) stream with
+//     non-temporal loads and stores, so they do not displace the keys in
+//     L2: with plain ones the q fold read at ~3.1 TB/s and the kernel took
+//     144 us at 8192 x 8192, against 22 us for the fold and 108 us.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -118,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void score_prefill_fold_kernel(
                 for (int u = 0; u < 16; ++u) {
                     const int h = 4 * u + hq;
                     const bool ok = row_ok(i) && h < H;
-                    v[rr][u] = ok ? *reinterpret_cast<const u32x4*>(q + ((size_t)r * H + h) * 128 + 8 * db)
+                    v[rr][u] = ok ? __builtin_nontemporal_load(
+                                        reinterpret_cast<const u32x4*>(q + ((size_t)r * H + h) * 128 + 8 * db))
                                   : u32x4{0u, 0u, 0u, 0u};
                     wv[rr][u] = w_sh[i][4 * u + hq];  // 0 for rows and heads out of range
                 }
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void score_prefill_fold_kernel(
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const int i = 16 * m + 8 * (j / 4) + 4 * g + j % 4;
-                        if (row_ok(i)) scores[(size_t)grow(i) * S_max + s] = mb;
+                        if (row_ok(i)) __builtin_nontemporal_store(mb, &scores[(size_t)grow(i) * S_max + s]);
                     }
             continue;
         }
@@ -246,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void score_prefill_fold_kernel(
                 for (int j = 0; j < 8; ++j) {
                     const int i = 16 * m + 8 * (j / 4) + 4 * g + j % 4;
                     if (row_ok(i))
-                        scores[(size_t)grow(i) * S_max + s] = s < nv_r[m][j] ? c[m][j] + c[m][j + 8] : mb;
+                        __builtin_nontemporal_store(s < nv_r[m][j] ? c[m][j] + c[m][j + 8] : mb,
+                                                    &scores[(size_t)grow(i) * S_max + s]);
                 }
     }
 }
