@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(
     // store 64 scores starting at key s0 (lane l covers s0 + l)
     auto put64 = [&](const int s0, const float v) {
         const int s = s0 + lane;
-        if (q_ok && s >= 0 && s < S_max) out[s] = (s < nv) ? v : mb;
+        if (q_ok && s >= 0 && s < S_max) __builtin_nontemporal_store((s < nv) ? v : mb, out + s);
     };
     // At the start of stage st the scores of sub-tiles 4 st - 5 .. 4 st - 2 are
     // final (slot 3 holds 4 st - 5, slot j < 3 holds 4 st - 4 + j); they go
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(
         const float va = g ? sc[0] : sc[3];
         const float vb = g ? sc[2] : sc[1];
         if (k0 >= 0 && k0 + 4 * kSub <= nv) {  // uniform: all 128 keys attendable
-            out[k0 + lane] = va;
-            out[k0 + 2 * kSub + lane] = vb;
+            __builtin_nontemporal_store(va, out + k0 + lane);
+            __builtin_nontemporal_store(vb, out + k0 + 2 * kSub + lane);
         } else {
             put64(k0, va);
             put64(k0 + 2 * kSub, vb);
