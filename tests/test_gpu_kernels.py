@@ -275,8 +275,12 @@ def test_attn_tiny_decode_shape(dsa):
     _attn_case(dsa, "tiny", q, kv, sk, idx, 192 ** -0.5, 128)
 
 
-def test_attn_full_decode_shape_split(dsa):
-    q, kv, sk, idx = _attn_inputs(2, 2, 1, 128, 576, 512, 3000, 1152, masked=0.05)
+# B = 2: fewer tokens than XCDs; B = 13: more, not a multiple of 8 (the split-combine places whole
+# tokens per XCD, so the last XCDs get a partial run or none); both run 8 splits of the list
+@pytest.mark.parametrize("B", [2, 13])
+def test_attn_full_decode_shape_split(dsa, B):
+    q, kv, sk, idx = _attn_inputs(2 + B, B, 1, 128, 576, 512, 3000, 1152, masked=0.05)
+    assert dsa.load_library().dsa_sparse_attn_workspace_size(B, 1, 128, 512, 1152) > 0  # split path
     _, rel = _attn_case(dsa, "mla-shaped split", q, kv, sk, idx, 576 ** -0.5, 512)
     assert rel < 2e-2
 
