@@ -13,7 +13,8 @@
 // contract allows.
 //
 //  * chunked path (few long rows, the decode case): rows are cut into
-//    4096-slot chunks so the whole chip works on them.
+//    4096-slot chunks (2048 when that leaves fewer than 512 workgroups) so
+//    the whole chip works on them.
 //      topk_clear   zero the per-row histograms / counters in the workspace
 //                   (the decode step has its scorer do this instead)
 //      topk_hist    per chunk: LDS histogram of the first digit, flushed to
@@ -45,7 +46,9 @@ namespace dsa {
 namespace {
 
 constexpr int kBins = 4096;  // first / second digit: 12 bits
-constexpr int kChunk = 4096;  // slots per workgroup in the chunked path
+constexpr int kChunk = 4096;  // slots per workgroup in the chunked path (rows longer than this are chunked)
+constexpr int kChunkSmall = 2048;  // ... when 4096-slot chunks would give fewer than kSmallGridWgs workgroups
+constexpr int kSmallGridWgs = 512;
 constexpr int kChunkThreads = 256;
 constexpr int kRowThreads = 1024;
 constexpr int kCoarse = 256;  // top 8 key bits: sign + 7 exponent bits
@@ -310,6 +313,7 @@ __global__ __launch_bounds__(256) void topk_clear_kernel(uint32_t* __restrict__ 
     if (i < n_words) ws[i] = 0u;
 }
 
+template <int CHUNK>
 __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
     int32_t k, uint32_t* __restrict__ ghist)
@@ -317,12 +321,12 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     static_assert(kChunkThreads == kCoarse, "one thread per coarse bin");
     __shared__ int hist[kBins];
     const int r = blockIdx.y;
-    const int s0 = blockIdx.x * kChunk;
+    const int s0 = blockIdx.x * CHUNK;
     const float* __restrict__ row = scores + (size_t)r * S_max;
     // The chunk's scores are loaded before n_valid is known (every slot
     // below S_max is readable), so the position lookup overlaps them.
-    constexpr int kPer = kChunk / kChunkThreads;  // 16 slots per thread: loads first, then LDS atomics
-    const int sl = min(s0 + kChunk, S_max);
+    constexpr int kPer = CHUNK / kChunkThreads;  // slots per thread: loads first, then LDS atomics
+    const int sl = min(s0 + CHUNK, S_max);
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     }
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     if (nv <= k || s0 >= nv) return;  // uniform
-    const int s1 = min(s0 + kChunk, nv);
+    const int s1 = min(s0 + CHUNK, nv);
     for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -384,6 +388,7 @@ __device__ void row_threshold(const uint32_t* __restrict__ gh, uint32_t coarse, 
     __syncthreads();
 }
 
+template <int CHUNK>
 __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
     int32_t k, int32_t window, uint32_t* __restrict__ ghist, int2* __restrict__ cand,
@@ -395,15 +400,15 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
 
     const int r = blockIdx.y;
     const int nchunks = gridDim.x;
-    const int s0 = blockIdx.x * kChunk;
+    const int s0 = blockIdx.x * CHUNK;
     const float* __restrict__ row = scores + (size_t)r * S_max;
     const int t = threadIdx.x;
     // Loads that do not depend on n_valid go first (every slot below S_max
     // is readable): this chunk's scores and this thread's coarse bin, so that
     // the position lookup, the scores and the threshold lookup share one
     // memory latency.
-    constexpr int kPer = kChunk / kChunkThreads;  // 16 slots per thread
-    const int sl = min(s0 + kChunk, S_max);
+    constexpr int kPer = CHUNK / kChunkThreads;  // slots per thread
+    const int sl = min(s0 + CHUNK, S_max);
     float v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -426,20 +431,20 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
         }
     if (nv <= k) {
         // every attendable slot is selected, in slot order; -1 pads the rest
-        for (int j = s0 + t; j < min(s0 + kChunk, k); j += kChunkThreads) {
+        for (int j = s0 + t; j < min(s0 + CHUNK, k); j += kChunkThreads) {
             const int s = j < nv ? j : -1;
             orow[j] = s < 0 ? -1 : emit(s, wstart);
             if (osc) osc[j] = s >= 0 ? row[s] : -INFINITY;
         }
         if (blockIdx.x == nchunks - 1)  // k may exceed the chunked range
-            for (int j = nchunks * kChunk + t; j < k; j += kChunkThreads) {
+            for (int j = nchunks * CHUNK + t; j < k; j += kChunkThreads) {
                 orow[j] = -1;
                 if (osc) osc[j] = -INFINITY;
             }
         return;
     }
 
-    const int s1 = min(s0 + kChunk, nv);
+    const int s1 = min(s0 + CHUNK, nv);
     uint32_t keys[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -605,10 +610,18 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
     int2* cand = reinterpret_cast<int2*>(ghist + (size_t)M * kHeaderWords);
     const int n_words = M * kHeaderWords;
     if (!header_zeroed) topk_clear_kernel<<<(n_words + 255) / 256, 256, 0, stream>>>(ghist, n_words);
-    const dim3 grid((S_max + kChunk - 1) / kChunk, M);
-    topk_hist_kernel<<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
-    topk_filter_kernel<<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window, ghist, cand,
-                                                           out_idx, out_scores);
+    // chunk size: 4096 slots, or 2048 when that would leave the chip short of workgroups
+    if ((long long)M * ((S_max + kChunk - 1) / kChunk) < kSmallGridWgs) {
+        const dim3 grid((S_max + kChunkSmall - 1) / kChunkSmall, M);
+        topk_hist_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
+        topk_filter_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
+                                                                            ghist, cand, out_idx, out_scores);
+    } else {
+        const dim3 grid((S_max + kChunk - 1) / kChunk, M);
+        topk_hist_kernel<kChunk><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
+        topk_filter_kernel<kChunk><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
+                                                                       ghist, cand, out_idx, out_scores);
+    }
     topk_resolve_kernel<<<M, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window, ghist, cand,
                                                          out_idx, out_scores);
     return hipGetLastError();
