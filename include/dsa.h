@@ -71,6 +71,7 @@ typedef enum dsa_key_dtype {
 #define DSA_INDEX_HEAD_DIM 128 /* indexer head_dim: [NKI-V32] Dimensions; [NKI-MX] usage */
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_ATTN_DIM 576
+#define DSA_MAX_ATTN_VDIM 512 /* value features: the output accumulator holds 32 heads x 512 per wave */
 
 /* Library version string, e.g. "0.1.0". */
 const char* dsa_version(void);
@@ -168,7 +169,7 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
  *   out       [B, S, Hq, Dv] bf16 output, device
  *   lse       [B, S, Hq] fp32 output or NULL, device
  *
- * Limits: Dqk % 32 == 0, 32 <= Dqk <= 576; Dv % 16 == 0, 16 <= Dv <= Dqk;
+ * Limits: Dqk % 32 == 0, 32 <= Dqk <= 576; Dv % 16 == 0, 16 <= Dv <= min(Dqk, 512);
  * B, S, Hq, K_top >= 1; S_kv >= 1; B * S <= 65535; one sequence's KV
  * (S_kv * Dqk * 2 bytes) below 2 GiB.  The workspace (size from
  * dsa_sparse_attn_workspace_size; 0 when there are enough query tokens to

@@ -19,16 +19,19 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
 HIP_SOURCES = ["score_decode.hip", "score_decode_heads.hip", "score_prefill.hip", "topk.hip", "sparse_attn.hip",
-               "cache_write.hip", "score_prefill_fold.hip"]
+               "sparse_attn_decode.hip", "sparse_attn_wide.hip", "cache_write.hip", "score_prefill_fold.hip"]
 CPP_SOURCES = ["dsa_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source device options.  The attention kernel keeps its 128-register
-# output accumulator in VGPRs (MFMA results written to VGPRs, read-only MFMA
-# operands free to live in AGPRs); otherwise the compiler copies the whole
-# accumulator between AGPRs and VGPRs on every block.
-EXTRA = {"sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source device options.  The decode attention kernel keeps its
+# 128-register output accumulator in VGPRs (MFMA results written to VGPRs,
+# read-only MFMA operands free to live in AGPRs); otherwise the compiler
+# copies the whole accumulator between AGPRs and VGPRs on every block.  The
+# wide attention kernel writes its QK products to VGPRs the same way (its
+# 256-register accumulator is pinned to AGPRs by the asm P.V products).
+EXTRA = {"sparse_attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "sparse_attn_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:

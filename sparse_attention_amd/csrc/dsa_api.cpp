@@ -40,7 +40,7 @@ dsa_status_t check_index_score(const void* q, const float* w, const void* k_cach
         if (M > 65535) return DSA_ERR_SHAPE;
     } else {
         if (k_dtype != DSA_KEY_BF16) return DSA_ERR_UNSUPPORTED;
-        if ((flags & DSA_SCORE_RELU) && (H > 64 || !dsa::score_prefill_available())) return DSA_ERR_UNSUPPORTED;
+        if ((flags & DSA_SCORE_RELU) && H > 64) return DSA_ERR_UNSUPPORTED;  // per-head MFMA path: 4 head tiles
         if ((long long)S_max * D * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's keys: 32-bit offsets
     }
     if (!aligned16(q) || !aligned16(k_cache)) return DSA_ERR_ALIGN;
@@ -63,7 +63,7 @@ dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx
     if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
     if (B < 1 || S < 1 || Hq < 1 || S_kv < 1 || K_top < 1) return DSA_ERR_SHAPE;
     if (Dqk < 32 || Dqk > DSA_MAX_ATTN_DIM || Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
-    if (Dv < 16 || Dv > Dqk || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
+    if (Dv < 16 || Dv > Dqk || Dv > DSA_MAX_ATTN_VDIM || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if ((long long)B * S > 65535) return DSA_ERR_SHAPE;
     if (!paged && (long long)S_kv * Dqk * 2 > INT32_MAX) return DSA_ERR_SHAPE;  // one sequence's KV: 32-bit offsets
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return DSA_ERR_ALIGN;
@@ -143,7 +143,7 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     if (a->window < 0 || a->window > a->S_max) return DSA_ERR_SHAPE;
     if (a->Hq < 1) return DSA_ERR_SHAPE;
     if (a->Dqk < 32 || a->Dqk > DSA_MAX_ATTN_DIM || a->Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
-    if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
+    if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv > DSA_MAX_ATTN_VDIM || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if (decode_paging(a)) {
         dsa::PageMap pm;
         const dsa_status_t ps = check_paging(decode_paging(a), a->S_max, &pm);

@@ -32,9 +32,6 @@ hipError_t launch_score_decode_heads(const void* q, const float* w, const void* 
                                      int32_t H, int32_t S_max, float scale, float* scores, uint32_t* zero_ptr,
                                      size_t zero_words, const PageMap* paging, hipStream_t stream);
 
-// Whether this build contains the prefill (per-head MFMA) scoring kernel.
-bool score_prefill_available();
-
 // Prefill indexer score with the identity activation: the heads folded into one
 // fp32 query per row (split into bf16 hi + lo MFMA operands); bf16 keys.
 hipError_t launch_score_prefill_fold(const void* q, const float* w, const void* k_cache, const int32_t* positions,
@@ -59,9 +56,22 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
                        int32_t valid_len, int32_t k, int32_t window, int32_t* out_idx, float* out_scores,
                        void* workspace, bool header_zeroed, hipStream_t stream);
 
-// Split count and partial-buffer size of the sparse attention launch.
-int sparse_attn_splits(int32_t B, int32_t S, int32_t Hq, int32_t K_top);
+// Partial-buffer size of the sparse attention launch (0 when the list is not split).
 size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
+
+// The two attention kernels behind launch_sparse_attn: many query tokens
+// (128-head workgroups fill the chip; no split, no workspace) and few (the
+// list split over workgroups, partial results in the workspace).
+bool sparse_attn_wide_fits(int32_t B, int32_t S, int32_t Hq);
+hipError_t launch_sparse_attn_wide(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
+                                   int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
+                                   int32_t K_top, float sm_scale, void* out, float* lse, const PageMap* paging,
+                                   hipStream_t stream);
+size_t sparse_attn_decode_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
+hipError_t launch_sparse_attn_decode(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
+                                     int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
+                                     int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
+                                     const PageMap* paging, hipStream_t stream);
 
 hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,

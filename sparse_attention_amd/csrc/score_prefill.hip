@@ -315,7 +315,6 @@ __global__ __launch_bounds__(kThreads, 2) void score_prefill_kernel(
 
 }  // namespace
 
-bool score_prefill_available() { return true; }
 
 hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cache, const int32_t* positions,
                                 int32_t valid_len, int32_t M, int32_t rows_per_seq, int32_t H, int32_t S_max,

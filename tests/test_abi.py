@@ -106,6 +106,9 @@ def test_sparse_attn_validation_and_workspace(lib):
     assert call(Dv=600) == ERR_UNSUPPORTED
     assert call(Dv=24) == ERR_UNSUPPORTED
     assert call(K=0) == ERR_SHAPE
+    # Value features above 512 are rejected (the attention kernels' accumulators hold at most 512)
+    assert call(Dqk=576, Dv=528) == ERR_UNSUPPORTED
+    assert call(Dqk=576, Dv=576) == ERR_UNSUPPORTED
     # Few tokens: the index list is split over workgroups and the partial
     # results (bf16 output per split + fp32 max and sum) live in the workspace.
     # 2 tokens x 2 head groups -> 8 splits (36 blocks of 32 entries, >= 4 per split)
@@ -113,6 +116,8 @@ def test_sparse_attn_validation_and_workspace(lib):
     assert need == 2 * 8 * 128 * 512 * 2 + 2 * 8 * 128 * 8
     # 64 decode tokens x 2 head groups -> 2 splits
     assert lib.dsa_sparse_attn_workspace_size(64, 1, 128, 512, 1152) == 64 * 2 * 128 * 512 * 2 + 64 * 2 * 128 * 8
+    # 256 tokens fill the chip with 128-head workgroups: the other kernel, no split, no workspace
+    assert lib.dsa_sparse_attn_workspace_size(256, 1, 128, 512, 1152) == 0
     # enough tokens to fill the chip: no split, no workspace
     assert lib.dsa_sparse_attn_workspace_size(1024, 1, 64, 512, 64) == 0
     # a short list (2 blocks) is not split

@@ -292,6 +292,18 @@ def test_attn_ktop_and_sink(dsa, K_top, sink):
     _attn_case(dsa, "K_top=%d sink=%s" % (K_top, sink), q, kv, sk, idx, 0.125, 64)
 
 
+# Value widths that end in half a 32-feature tile, head counts that are not a multiple of the
+# 32 heads of a wave, and both workgroup shapes: few tokens (waves share 32 heads and split
+# each block's entries; list split over workgroups) and 300 tokens (each wave owns 32 of a
+# workgroup's 128 heads and every entry).
+@pytest.mark.parametrize("B,S,Hq,Dqk,Dv", [(3, 1, 40, 96, 80), (2, 2, 8, 32, 16), (300, 1, 40, 96, 80),
+                                           (2, 150, 128, 576, 512), (1, 300, 130, 192, 128)])
+def test_attn_odd_shapes(dsa, B, S, Hq, Dqk, Dv):
+    q, kv, sk, idx = _attn_inputs(11 + Hq, B, S, Hq, Dqk, Dv, 600, 300, masked=0.1)
+    _, rel = _attn_case(dsa, "odd shape", q, kv, sk, idx, Dqk ** -0.5, Dv)
+    assert rel < 2e-2
+
+
 def test_attn_index_patterns(dsa):
     q, kv, sk, idx = _attn_inputs(4, 3, 2, 24, 128, 96, 700, 300, masked=0.1, dup=0.1, oob=0.05)
     idx[0, 0, :] = -1                 # all masked
@@ -306,6 +318,57 @@ def test_attn_peaked_softmax(dsa):
     q, kv, sk, idx = _attn_inputs(5, 2, 1, 64, 576, 512, 2000, 512)
     q = (q.float() * 8).to(torch.bfloat16)
     _, rel = _attn_case(dsa, "peaked", q, kv, sk, idx, 576 ** -0.5, 512)
+    assert rel < 2e-2
+
+
+@pytest.mark.parametrize("Hq,Dqk,Dv", [(128, 576, 512), (16, 192, 128), (24, 128, 96)])
+def test_attn_growing_logits(dsa, Hq, Dqk, Dv):
+    """Logits that keep growing along the list: every head shares a query component c, and the
+    listed rows are a_j * c / |c| + noise with a_j rising from 0 to 20, so the logit of the j-th
+    listed row grows by ~90 (log2 units) over the list.  A block maximum then outgrows the running
+    reference many times within each split, which the kernel handles by running the list again with
+    a raised reference.  The softmax ends up concentrated on the last rows."""
+    B, S_kv, K_top = 2, 2000, 1152
+    g = np.random.default_rng(71)
+    c = g.standard_normal(Dqk)
+    c *= 3.0 * Dqk ** 0.5 / np.linalg.norm(c)
+    q = c[None, None, None, :] + 0.3 * g.standard_normal((B, 1, Hq, Dqk))
+    a = np.linspace(0.0, 20.0, K_top)
+    rows = np.stack([g.choice(S_kv, size=K_top, replace=False) for _ in range(B)])
+    kv = 0.3 * g.standard_normal((B, S_kv, Dqk))
+    for b in range(B):
+        kv[b, rows[b]] += a[:, None] * (c / np.linalg.norm(c))[None, :]
+    idx = rows[:, None, :].astype(np.int32)
+    q = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(kv.astype(np.float32)).to(torch.bfloat16)
+    sk = torch.from_numpy(g.standard_normal(Hq).astype(np.float32))
+    _, rel = _attn_case(dsa, "growing logits", q, kv, sk, torch.from_numpy(idx), Dqk ** -0.5, Dv)
+    assert rel < 2e-2
+    # the same rows listed in falling order: the first block holds the maximum, no second pass
+    _, rel = _attn_case(dsa, "falling logits", q, kv, sk, torch.from_numpy(idx[..., ::-1].copy()), Dqk ** -0.5,
+                        Dv)
+    assert rel < 2e-2
+
+
+def test_attn_growing_logits_many_tokens(dsa):
+    """As test_attn_growing_logits with 300 query tokens of one sequence (the kernel for calls whose
+    tokens fill the chip): every token lists the same 512 rows in rising order of a_j, so the
+    reference max of every head is outgrown several times along the list."""
+    S, Hq, Dqk, Dv, S_kv, K_top = 300, 32, 192, 128, 1000, 512
+    g = np.random.default_rng(73)
+    c = g.standard_normal(Dqk)
+    c *= 3.0 * Dqk ** 0.5 / np.linalg.norm(c)
+    q = c[None, None, None, :] + 0.3 * g.standard_normal((1, S, Hq, Dqk))
+    a = np.linspace(0.0, 20.0, K_top)
+    rows = g.choice(S_kv, size=K_top, replace=False)
+    kv = 0.3 * g.standard_normal((1, S_kv, Dqk))
+    kv[0, rows] += a[:, None] * (c / np.linalg.norm(c))[None, :]
+    idx = np.broadcast_to(rows[None, None, :], (1, S, K_top)).astype(np.int32).copy()
+    idx[0, ::7, ::5] = -1  # some masked entries on some tokens
+    q = torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(kv.astype(np.float32)).to(torch.bfloat16)
+    sk = torch.from_numpy(g.standard_normal(Hq).astype(np.float32))
+    _, rel = _attn_case(dsa, "growing logits, many tokens", q, kv, sk, torch.from_numpy(idx), Dqk ** -0.5, Dv)
     assert rel < 2e-2
 
 
