@@ -28,14 +28,16 @@
  *     the caller, dense row-major in the layout stated, 16-byte aligned.
  *     The library never allocates, frees or keeps a pointer; scratch space
  *     is the caller's `workspace` (size from the matching *_workspace_size
- *     query, which needs no GPU).
+ *     query, which needs no GPU).  The one exception is
+ *     dsa_decode_step_static, whose scratch is a library-owned device array.
  *   - All work is enqueued on `stream` (NULL = the default stream); no call
  *     synchronises the host.
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error status no output has been touched.  DSA_ERR_LAUNCH reports a
  *     launch failure; faults during execution surface at the caller's next
  *     synchronisation.  No C++ exception crosses this interface.  Calls are
- *     thread-safe; the library holds no state.
+ *     thread-safe; the library holds no state beyond the scratch array of
+ *     dsa_decode_step_static and its device address per GPU.
  *   - bf16 = bfloat16; fp8 = OCP FP8 E4M3 ("e4m3fn", max 448) bytes.
  */
 #ifndef DSA_H_
@@ -256,6 +258,29 @@ typedef struct dsa_decode_args {
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args);
 dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * dsa_decode_step_static -- dsa_decode_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results as dsa_decode_step, but the step's scratch space is a
+ * library-owned device array of DSA_STATIC_SCRATCH_BYTES instead of a
+ * caller workspace; the caller still provides every input and output.
+ *
+ * The array exists once per GPU (the current device at the call), from the
+ * first call on that GPU until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams, or different
+ * host threads without ordering) race and must be serialised by the caller.
+ * Contents left by an earlier call are never read.
+ *
+ * Errors: as dsa_decode_step for invalid arguments; DSA_ERR_WORKSPACE when
+ * dsa_decode_step_workspace_size(args) exceeds DSA_STATIC_SCRATCH_BYTES
+ * (pass scores / index_list outputs to shrink it); DSA_ERR_LAUNCH when the
+ * array's device address cannot be obtained or a launch fails.
+ */
+#define DSA_STATIC_SCRATCH_BYTES ((size_t)128 << 20) /* 128 MiB per GPU */
+dsa_status_t dsa_decode_step_static(const dsa_decode_args_t* args, hipStream_t stream);
 
 
 /* dsa_index_score over a paged key cache, one query row per sequence

@@ -98,6 +98,8 @@ def load_library(path: Optional[str] = None):
     lib.dsa_decode_step_workspace_size.argtypes = [ctypes.POINTER(_DecodeArgs)]
     lib.dsa_decode_step.restype = st
     lib.dsa_decode_step.argtypes = [ctypes.POINTER(_DecodeArgs), vp, sz, vp]
+    lib.dsa_decode_step_static.restype = st
+    lib.dsa_decode_step_static.argtypes = [ctypes.POINTER(_DecodeArgs), vp]
     pp = ctypes.POINTER(_PagedCache)
     lib.dsa_index_score_paged.restype = st
     lib.dsa_index_score_paged.argtypes = [vp, vp, vp, vp, st, pp, vp, i32, i32, i32, i32, i32, f32, u32, vp, vp]
@@ -249,13 +251,19 @@ def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, wit
     return (out, lse) if with_lse else out
 
 
+DSA_STATIC_SCRATCH_BYTES = 128 << 20
+
+
 class DecodeStep:
-    """Reusable dsa_decode_step call: validates shapes once, owns the workspace and outputs."""
+    """Reusable dsa_decode_step call: validates shapes once, owns the workspace and outputs.
+
+    With ``static_scratch`` the step calls dsa_decode_step_static instead: no workspace is allocated and the
+    library's per-GPU scratch array (DSA_STATIC_SCRATCH_BYTES) is used; calls on one GPU must not overlap."""
 
     def __init__(self, index_q, index_w, k_cache, *, positions=None, valid_len: int = -1, index_scale: float,
                  index_topk: int, window: int, q, kv, attn_sink, sm_scale: float, dv: int, k_scale=None,
                  keep_scores: bool = True, keep_index_list: bool = True, relu: bool = False,
-                 paging: Optional[Paging] = None, s_max: Optional[int] = None):
+                 paging: Optional[Paging] = None, s_max: Optional[int] = None, static_scratch: bool = False):
         _dev(index_q, "index_q", (torch.bfloat16,))
         _dev(index_w, "index_w", (torch.float32,))
         _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -298,11 +306,16 @@ class DecodeStep:
         a.paging = None if paging is None else ctypes.addressof(paging.struct)
         self._args = a
         lib = load_library()
+        self.static_scratch = bool(static_scratch)
         self._nws = lib.dsa_decode_step_workspace_size(ctypes.byref(a))
-        self._ws = _workspace(self._nws, dev)
+        self._ws = None if self.static_scratch else _workspace(self._nws, dev)
 
     def __call__(self):
-        st = load_library().dsa_decode_step(ctypes.byref(self._args), _ptr(self._ws), self._nws, _stream())
+        lib = load_library()
+        if self.static_scratch:
+            _check("dsa_decode_step_static", lib.dsa_decode_step_static(ctypes.byref(self._args), _stream()))
+            return self.out
+        st = lib.dsa_decode_step(ctypes.byref(self._args), _ptr(self._ws), self._nws, _stream())
         _check("dsa_decode_step", st)
         return self.out
 

@@ -181,6 +181,13 @@ dsa_status_t check_cache_write(const void* k_new, int32_t T, int32_t rows_per_se
 
 }  // namespace
 
+dsa_status_t dsa::decode_step_check(const dsa_decode_args_t* args, size_t* need)
+{
+    const dsa_status_t s = check_decode(args);
+    if (s == DSA_OK) *need = layout_decode(args).total;
+    return s;
+}
+
 extern "C" {
 
 const char* dsa_version(void) { return "0.1.0"; }

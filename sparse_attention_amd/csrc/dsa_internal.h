@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dsa.h"
+
 namespace dsa {
 
 // Page pool addressing of a paged key or KV store: slot s of sequence r is
@@ -83,5 +85,9 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_s
 hipError_t launch_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, const int32_t* positions,
                               bool key_fp8, bool qdq, bool round_scale, void* k_cache, float* k_scale,
                               int32_t S_max, const PageMap* paging, hipStream_t stream);
+
+// Validates a decode step's arguments as dsa_decode_step does and, when they
+// are valid, stores the workspace bytes the step needs in *need.
+dsa_status_t decode_step_check(const dsa_decode_args_t* args, size_t* need);
 
 }  // namespace dsa

@@ -182,6 +182,37 @@ def test_decode_step_validation(lib):
     assert lib.dsa_decode_step(ctypes.byref(a), _p(A), ws, None) == ERR_NULL
 
 
+def test_decode_step_static_validation(lib):
+    """The allocation-free decode step validates like dsa_decode_step and rejects shapes whose
+    scratch exceeds the library's array before touching any device."""
+    import sparse_attention_amd as m
+
+    assert lib.dsa_decode_step_static(None, None) == ERR_NULL
+    a = m._DecodeArgs()
+    a.struct_size = ctypes.sizeof(m._DecodeArgs)
+    for name in ("index_q", "index_w", "k_cache", "q", "kv", "out"):
+        setattr(a, name, A)
+    a.B, a.H, a.S_max, a.index_topk, a.window = 4, 64, 4096, 1024, 128
+    a.Hq, a.Dqk, a.Dv, a.valid_len = 128, 576, 512, -1
+    a.window = -1
+    assert lib.dsa_decode_step_static(ctypes.byref(a), None) == ERR_SHAPE
+    a.window, a.Dv = 128, 528
+    assert lib.dsa_decode_step_static(ctypes.byref(a), None) == ERR_UNSUPPORTED
+    a.Dv, a.q = 512, None
+    assert lib.dsa_decode_step_static(ctypes.byref(a), None) == ERR_NULL
+    a.q = A
+    # 1024 sequences x 65536 slots with scores and list kept in scratch: beyond the 128 MiB array
+    a.B, a.S_max = 1024, 65536
+    assert lib.dsa_decode_step_workspace_size(ctypes.byref(a)) > m.DSA_STATIC_SCRATCH_BYTES
+    assert lib.dsa_decode_step_static(ctypes.byref(a), None) == ERR_WORKSPACE
+    # the full decode step shape (64 x 65536, scores kept in scratch) fits
+    a.B = 64
+    assert lib.dsa_decode_step_workspace_size(ctypes.byref(a)) <= m.DSA_STATIC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    assert re.search(r"#define DSA_STATIC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", text)
+    assert m.DSA_STATIC_SCRATCH_BYTES == 128 << 20
+
+
 def test_paged_validation(lib):
     import sparse_attention_amd as m
 
