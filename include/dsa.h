@@ -72,6 +72,7 @@ typedef enum dsa_key_dtype {
 
 #define DSA_INDEX_HEAD_DIM 128 /* indexer head_dim: [NKI-V32] Dimensions; [NKI-MX] usage */
 #define DSA_MAX_TOPK 2048
+#define DSA_MAX_TOPK_SLOTS (1 << 24) /* slots per row of dsa_topk / dsa_decode_step */
 #define DSA_MAX_ATTN_DIM 576
 #define DSA_MAX_ATTN_VDIM 512 /* value features: the output accumulator holds 32 heads x 512 per wave */
 
@@ -140,7 +141,11 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
  *               -inf where the index is -1 ([NEMO-DSV4]
  *               extract_indexer_topk_scores_torch)
  *
- * Limits: 1 <= index_topk <= DSA_MAX_TOPK; M >= 1; S_max >= 1.
+ * The output is deterministic: the same scores give the same row, column
+ * for column, on every call (ties at the boundary included).
+ *
+ * Limits: 1 <= index_topk <= DSA_MAX_TOPK; M >= 1;
+ * 1 <= S_max <= DSA_MAX_TOPK_SLOTS.
  */
 size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk);
 dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
@@ -224,6 +229,10 @@ typedef struct dsa_paged_cache {
  * With paging != NULL, k_cache / k_scale and kv are page pools (see
  * dsa_paged_cache_t) sharing one block table, and S_max is the logical slot
  * count of every sequence.
+ *
+ * Every stage is deterministic (the index list included, column for
+ * column), so the same inputs give bitwise-identical outputs on every call.
+ * Limits: those of the three stages; B <= 65535; S_max <= DSA_MAX_TOPK_SLOTS.
  */
 typedef struct dsa_decode_args {
     size_t struct_size;

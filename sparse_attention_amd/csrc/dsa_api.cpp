@@ -51,7 +51,7 @@ dsa_status_t check_index_score(const void* q, const float* w, const void* k_cach
 dsa_status_t check_topk(const float* scores, int32_t M, int32_t S_max, int32_t k, const int32_t* topk_idx)
 {
     if (!scores || !topk_idx) return DSA_ERR_NULL;
-    if (M < 1 || S_max < 1) return DSA_ERR_SHAPE;
+    if (M < 1 || S_max < 1 || S_max > DSA_MAX_TOPK_SLOTS) return DSA_ERR_SHAPE;
     if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
     if (!aligned16(scores) || !aligned16(topk_idx)) return DSA_ERR_ALIGN;
     return DSA_OK;
@@ -137,7 +137,7 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     if (a->k_dtype != DSA_KEY_BF16 && a->k_dtype != DSA_KEY_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
     if (a->k_dtype == DSA_KEY_FP8_E4M3 && !a->k_scale) return DSA_ERR_NULL;
     if (a->k_dtype == DSA_KEY_BF16 && a->k_scale) return DSA_ERR_SHAPE;
-    if (a->B < 1 || a->B > 65535 || a->H < 1 || a->S_max < 1) return DSA_ERR_SHAPE;
+    if (a->B < 1 || a->B > 65535 || a->H < 1 || a->S_max < 1 || a->S_max > DSA_MAX_TOPK_SLOTS) return DSA_ERR_SHAPE;
     if (a->H > 128) return DSA_ERR_UNSUPPORTED;
     if (a->index_topk < 1 || a->index_topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
     if (a->window < 0 || a->window > a->S_max) return DSA_ERR_SHAPE;

@@ -9,8 +9,13 @@
 // scores (digits: key bits 31..20, 19..8, 7..0).  After each digit the
 // bucket holding the k-th largest key is found by a suffix scan of the
 // histogram; keys above it are selected, keys inside it stay candidates.
-// Ties at the final threshold are taken in arrival order, which the set
-// contract allows.
+//
+// The output is deterministic: every position is fixed by prefix sums over
+// threads, waves and chunks in a fixed order (no atomic decides an output
+// position), so repeated calls on the same scores return the same row,
+// column for column, and ties at the final threshold are broken the same
+// way every time.  The set contract would allow any order; a fixed one
+// makes the attention that sums over the list bitwise reproducible.
 //
 //  * chunked path (few long rows, the decode case): rows are cut into
 //    4096-slot chunks (2048 when that leaves fewer than 512 workgroups) so
@@ -22,16 +27,19 @@
 //                   bins): 4096 fine bins and 256 coarse bins (top 8 bits)
 //                   so later stages find the threshold bin cheaply
 //      topk_filter  per chunk: threshold bucket from the row histogram;
-//                   slots above it are written out directly (one global
-//                   atomic per workgroup reserves the output range), slots
-//                   in it are appended to the row's (key, slot) list;
-//                   chunk 0 also records the row's threshold bin and the
-//                   count above it for the resolve;
-//      topk_resolve one workgroup per row runs the two remaining digits over
-//                   the candidates.  Kernel boundaries make the other
-//                   workgroups' writes visible; an in-kernel "last
-//                   workgroup" hand-off would need a device-scope fence,
-//                   which on these multi-XCD parts writes back the L2.
+//                   the chunk's (key, slot) pairs above it, then those in
+//                   it, go to the chunk's own region of the candidate
+//                   buffer (positions from a workgroup scan), and their two
+//                   counts to the row's count table; chunk 0 also records
+//                   the row's threshold bin.  No global atomics;
+//      topk_resolve one workgroup per row: prefix sums of the chunk counts
+//                   place every chunk's slots above the threshold bin in
+//                   the output in chunk order, then the two remaining
+//                   digits run over the threshold bin's candidates.  Kernel
+//                   boundaries make the other workgroups' writes visible; an
+//                   in-kernel "last workgroup" hand-off would need a
+//                   device-scope fence, which on these multi-XCD parts
+//                   writes back the L2.
 //  * row path (many short rows, e.g. prefill): one workgroup per row runs
 //    all digits with LDS histograms; rows of up to 8192 slots are read once
 //    into LDS, longer rows are re-read from memory per digit.
@@ -52,11 +60,12 @@ constexpr int kSmallGridWgs = 512;
 constexpr int kChunkThreads = 256;
 constexpr int kRowThreads = 1024;
 constexpr int kCoarse = 256;  // top 8 key bits: sign + 7 exponent bits
-constexpr int kCtrl = 4;      // per-row words: above-threshold count, candidate count, threshold bin, count above it
+constexpr int kCtrl = 4;      // per-row words: [2] = threshold bin of the first digit (others unused)
 constexpr int kHeaderWords = kBins + kCoarse + kCtrl;  // per-row words zeroed before each call
 constexpr int kResolveCap = 8192;  // candidates resolved from LDS; more are re-read from HBM
 constexpr int kRowLdsThreads = 512;
 constexpr int kRowCap = 8192;      // row path: rows up to this many slots are held in LDS
+constexpr int kMaxChunks = 4096;   // chunks per row the resolve's LDS prefix tables hold (rows up to 2^24 slots)
 
 // ---------------------------------------------------------------- helpers
 
@@ -108,6 +117,46 @@ __device__ void find_bucket(const int* hist, int nbins, int need, int* wave_tot,
 
 __device__ __forceinline__ int emit(int s, int wstart) { return s >= wstart ? -1 : s; }
 
+__device__ __forceinline__ float key_to_f32(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Deterministic compaction of one round of a workgroup of NT threads: this
+// thread's rank among the round's `gt` threads and among its `eq` threads
+// (lower waves first, then lower lanes), and the round's totals.  wcnt is a
+// [2][2][NT / 64] LDS table used alternately by successive rounds (`parity`),
+// so one barrier per round suffices.
+template <int NT>
+__device__ __forceinline__ void round_ranks(bool gt, bool eq, int (*wcnt)[2][NT / 64], int parity, int* rank_gt,
+                                            int* rank_eq, int* tot_gt, int* tot_eq)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
+    const uint64_t bg = __ballot(gt);
+    const uint64_t be = __ballot(eq);
+    if (lane == 0) {
+        wcnt[parity][0][wave] = __popcll(bg);
+        wcnt[parity][1][wave] = __popcll(be);
+    }
+    __syncthreads();
+    int bgt = 0, beq = 0, tg = 0, te = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int a = wcnt[parity][0][w];
+        const int b = wcnt[parity][1][w];
+        bgt += w < wave ? a : 0;
+        beq += w < wave ? b : 0;
+        tg += a;
+        te += b;
+    }
+    *rank_gt = bgt + __popcll(bg & lt);
+    *rank_eq = beq + __popcll(be & lt);
+    *tot_gt = tg;
+    *tot_eq = te;
+}
+
 // ---------------------------------------------------------------- row path
 
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
@@ -116,7 +165,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 {
     __shared__ int hist[kBins];
     __shared__ int wave_tot[kRowThreads / 64];
-    __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq;
+    __shared__ int wcnt[2][2][kRowThreads / 64];
+    __shared__ int sh_digit, sh_above;
 
     const int r = blockIdx.x;
     const int nv = n_valid_of(positions, valid_len, r, S_max);
@@ -164,33 +214,38 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         if (exact) break;
     }
 
-    if (t == 0) {
-        cnt_gt = 0;
-        cnt_eq = 0;
-    }
-    __syncthreads();
     const int n_gt = k - remaining;
-    for (int s = t; s < nv; s += kRowThreads) {
-        const float v = row[s];
+    int carry_gt = 0, carry_eq = 0, parity = 0;
+    for (int s0 = 0; s0 < nv; s0 += kRowThreads) {  // uniform trip count
+        const int s = s0 + t;
+        const float v = s < nv ? row[s] : 0.f;
         const uint32_t km = f32_order_key(v) & pmask;
+        const bool gt = s < nv && km > prefix;
+        const bool eq = s < nv && km == prefix;
+        int rg, re, tg, te;
+        round_ranks<kRowThreads>(gt, eq, wcnt, parity, &rg, &re, &tg, &te);
         int pos = -1;
-        if (km > prefix) {
-            pos = atomicAdd(&cnt_gt, 1);
-        } else if (km == prefix) {
-            const int tk = atomicAdd(&cnt_eq, 1);
+        if (gt) {
+            pos = carry_gt + rg;
+        } else if (eq) {
+            const int tk = carry_eq + re;
             if (tk < remaining) pos = n_gt + tk;
         }
         if (pos >= 0) {
             orow[pos] = emit(s, wstart);
             if (osc) osc[pos] = v;
         }
+        carry_gt += tg;
+        carry_eq += te;
+        parity ^= 1;
     }
 }
 
 // Row path for rows of at most kRowCap slots (16-byte aligned): the row is
 // read once with 16-byte loads into LDS as order keys, building the first
 // digit's histogram on the way; later digits and the output pass run on LDS.
-// Outputs are compacted per wave (ballot + one LDS atomic per wave).
+// Outputs are compacted per round of NT slots (wave ballots, the waves'
+// counts summed through LDS), in slot order.
 __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
     int32_t k, int32_t window, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
@@ -199,7 +254,8 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t keys[kRowCap];
     __shared__ int hist[kBins];
     __shared__ int wave_tot[NT / 64];
-    __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq;
+    __shared__ int wcnt[2][2][NT / 64];
+    __shared__ int sh_digit, sh_above;
 
     const int r = (int)(gridDim.x - 1 - blockIdx.x);  // long rows first
     const int nv = n_valid_of(positions, valid_len, r, S_max);
@@ -209,7 +265,6 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     int32_t* __restrict__ orow = out_idx + (size_t)r * width;
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
     const int t = threadIdx.x;
-    const int lane = t & 63;
 
     for (int i = t; i < window; i += NT) {
         const int p = wstart + i;
@@ -266,14 +321,9 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
         if (exact) break;
     }
 
-    if (t == 0) {
-        cnt_gt = 0;
-        cnt_eq = 0;
-    }
-    __syncthreads();
     const int n_gt = k - remaining;
-    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes below this one
-    for (int s0 = 0; s0 < nv; s0 += NT) {
+    int carry_gt = 0, carry_eq = 0, parity = 0;
+    for (int s0 = 0; s0 < nv; s0 += NT) {  // uniform trip count
         const int s = s0 + t;
         uint32_t key = 0;
         bool gt = false, eq = false;
@@ -282,26 +332,22 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
             gt = (key & pmask) > prefix;
             eq = (key & pmask) == prefix;
         }
-        const uint64_t bg = __ballot(gt);
-        const uint64_t be = __ballot(eq);
-        int bgt = 0, beq = 0;
-        if (lane == 0) {
-            if (bg) bgt = atomicAdd(&cnt_gt, __popcll(bg));
-            if (be) beq = atomicAdd(&cnt_eq, __popcll(be));
-        }
-        bgt = __shfl(bgt, 0, 64);
-        beq = __shfl(beq, 0, 64);
+        int rg, re, tg, te;
+        round_ranks<NT>(gt, eq, wcnt, parity, &rg, &re, &tg, &te);
         int pos = -1;
         if (gt) {
-            pos = bgt + __popcll(bg & lt);
+            pos = carry_gt + rg;
         } else if (eq) {
-            const int tk = beq + __popcll(be & lt);
+            const int tk = carry_eq + re;
             if (tk < remaining) pos = n_gt + tk;
         }
         if (pos >= 0) {
             orow[pos] = emit(s, wstart);
-            if (osc) osc[pos] = __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+            if (osc) osc[pos] = key_to_f32(key);
         }
+        carry_gt += tg;
+        carry_eq += te;
+        parity ^= 1;
     }
 }
 
@@ -391,12 +437,12 @@ __device__ void row_threshold(const uint32_t* __restrict__ gh, uint32_t coarse, 
 template <int CHUNK>
 __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
-    int32_t k, int32_t window, uint32_t* __restrict__ ghist, int2* __restrict__ cand,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
+    int32_t k, int32_t window, uint32_t* __restrict__ ghist, int2* __restrict__ counts, int32_t n_counts,
+    int2* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
 {
     __shared__ int scratch[kCoarse];
     __shared__ int wave_tot[kChunkThreads / 64];
-    __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq, base_gt, base_eq;
+    __shared__ int sh_digit, sh_above;
 
     const int r = blockIdx.y;
     const int nchunks = gridDim.x;
@@ -417,7 +463,6 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
     }
     uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
     const uint32_t coarse = gh[kBins + t];  // kChunkThreads == kCoarse
-
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     const int width = k + window;
     const int wstart = nv - window;
@@ -443,6 +488,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
             }
         return;
     }
+    if (s0 >= nv) return;  // uniform: the resolve reads only chunks below n_valid (chunk 0 always runs)
 
     const int s1 = min(s0 + CHUNK, nv);
     uint32_t keys[kPer];
@@ -451,17 +497,9 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
         const int s = s0 + i * kChunkThreads + t;
         keys[i] = (s < s1) ? f32_order_key(v[i]) : 0u;
     }
-    if (t == 0) {
-        cnt_gt = 0;
-        cnt_eq = 0;
-    }
     row_threshold(gh, coarse, k, scratch, wave_tot, &sh_digit, &sh_above);
     const uint32_t d1 = (uint32_t)sh_digit;
-    uint32_t* __restrict__ ctrl = gh + kBins + kCoarse;
-    if (blockIdx.x == 0 && t == 0) {  // for the resolve (visible after this kernel)
-        ctrl[2] = d1;
-        ctrl[3] = (uint32_t)sh_above;
-    }
+    if (blockIdx.x == 0 && t == 0) gh[kBins + kCoarse + 2] = d1;  // for the resolve (visible after this kernel)
 
     int my_gt = 0, my_eq = 0;
 #pragma unroll
@@ -471,69 +509,120 @@ __global__ __launch_bounds__(kChunkThreads) void topk_filter_kernel(
         my_gt += (in && dg > d1) ? 1 : 0;
         my_eq += (in && dg == d1) ? 1 : 0;
     }
-    int off_gt = my_gt ? atomicAdd(&cnt_gt, my_gt) : 0;
-    int off_eq = my_eq ? atomicAdd(&cnt_eq, my_eq) : 0;
-    __syncthreads();
-    if (t == 0) {
-        base_gt = cnt_gt ? (int)atomicAdd(&ctrl[0], (uint32_t)cnt_gt) : 0;
-        base_eq = cnt_eq ? (int)atomicAdd(&ctrl[1], (uint32_t)cnt_eq) : 0;
-    }
-    __syncthreads();
-    off_gt += base_gt;
-    off_eq += base_eq;
-    int2* __restrict__ crow = cand + (size_t)r * S_max;
+    // both counts in one scan: at most CHUNK <= 2^15 each, so the halves never carry into each other
+    const int packed = my_gt | (my_eq << 16);
+    const int incl = block_inclusive_scan<kChunkThreads>(packed, wave_tot);
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < kChunkThreads / 64; ++i) tot += wave_tot[i];
+    const int excl = incl - packed;
+    const int tot_gt = tot & 0xFFFF;
+    int off_gt = excl & 0xFFFF;
+    int off_eq = tot_gt + (excl >> 16);
+    // the chunk's region: slots above the threshold bin first, then the bin's candidates
+    int2* __restrict__ region = cand + (size_t)r * S_max + s0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int s = s0 + i * kChunkThreads + t;
         if (s >= s1) continue;
         const uint32_t dg = keys[i] >> 20;
-        if (dg > d1) {
-            orow[off_gt] = emit(s, wstart);
-            if (osc) osc[off_gt] = v[i];
-            ++off_gt;
-        } else if (dg == d1) {
-            crow[off_eq++] = make_int2((int)keys[i], s);
-        }
+        if (dg > d1) region[off_gt++] = make_int2((int)keys[i], s);
+        else if (dg == d1) region[off_eq++] = make_int2((int)keys[i], s);
     }
+    if (t == 0) counts[(size_t)r * n_counts + blockIdx.x] = make_int2(tot_gt, tot >> 16);
 }
 
-// Resolve the threshold bucket of each row among its (key, slot) candidates:
-// the two remaining digits, from LDS when the candidates fit.
+// Per row: the chunks' slots above the threshold bin go to the output in
+// chunk order; the threshold bin's candidates (gathered in chunk order, in
+// LDS when they fit) are resolved with the two remaining digits and placed
+// by per-round ranks.
+template <int CHUNK>
 __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
-    int32_t k, int32_t window, uint32_t* __restrict__ ghist, const int2* __restrict__ cand,
-    int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
+    int32_t k, int32_t window, const uint32_t* __restrict__ ghist, const int2* __restrict__ counts,
+    int32_t n_counts, const int2* __restrict__ cand, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
 {
+    constexpr int NT = kChunkThreads;
     __shared__ int hist[kBins];
     __shared__ int2 lcand[kResolveCap];
-    __shared__ int wave_tot[kChunkThreads / 64];
-    __shared__ int sh_digit, sh_above, cnt_gt, cnt_eq;
+    __shared__ int pre_gt[kMaxChunks + 1];  // exclusive prefix sums of the chunks' counts
+    __shared__ int pre_eq[kMaxChunks + 1];
+    __shared__ int wave_tot[NT / 64];
+    __shared__ int wcnt[2][2][NT / 64];
+    __shared__ int sh_digit, sh_above;
 
     const int r = blockIdx.x;
-    // the threshold bin and the count above it, as the filter's chunk 0
-    // found them, and the candidate count (the filter's running total);
-    // read together with the position
-    const uint32_t* __restrict__ ctrl = ghist + (size_t)r * kHeaderWords + kBins + kCoarse;
-    const int n_cand = (int)ctrl[1];
-    const uint32_t d1 = ctrl[2];
-    const int above = (int)ctrl[3];
+    const uint32_t d1 = ghist[(size_t)r * kHeaderWords + kBins + kCoarse + 2];  // read with the position
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     if (nv <= k) return;  // uniform
     const int width = k + window;
     const int wstart = nv - window;
-    const float* __restrict__ row = scores + (size_t)r * S_max;
     int32_t* __restrict__ orow = out_idx + (size_t)r * width;
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
     const int t = threadIdx.x;
+    const int nch = (nv + CHUNK - 1) / CHUNK;  // chunks the filter filled (<= kMaxChunks)
+    const int2* __restrict__ crow = counts + (size_t)r * n_counts;
+    const int2* __restrict__ rbase = cand + (size_t)r * S_max;
 
-    const bool in_lds = n_cand <= kResolveCap;
-    const int2* __restrict__ crow = cand + (size_t)r * S_max;
-    if (in_lds)
-        for (int i = t; i < n_cand; i += kChunkThreads) lcand[i] = crow[i];
+    // prefix sums of the chunk counts, 256 chunks per round
+    int carry_gt = 0, carry_eq = 0;
+    for (int c0 = 0; c0 < nch; c0 += NT) {
+        const int c = c0 + t;
+        const int2 n = c < nch ? crow[c] : make_int2(0, 0);
+        const int ig = block_inclusive_scan<NT>(n.x, wave_tot);
+        int tg = 0;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) tg += wave_tot[i];
+        __syncthreads();
+        const int ie = block_inclusive_scan<NT>(n.y, wave_tot);
+        int te = 0;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) te += wave_tot[i];
+        if (c < nch) {
+            pre_gt[c + 1] = carry_gt + ig;
+            pre_eq[c + 1] = carry_eq + ie;
+        }
+        carry_gt += tg;
+        carry_eq += te;
+        __syncthreads();
+    }
+    if (t == 0) {
+        pre_gt[0] = 0;
+        pre_eq[0] = 0;
+    }
     __syncthreads();
-    auto cand_at = [&](int i) -> int2 { return in_lds ? lcand[i] : crow[i]; };
+    const int total_gt = carry_gt;  // slots above the threshold bin
+    const int n_cand = carry_eq;    // slots in it
+    // chunk holding entry j of a prefix table: the largest c with pre[c] <= j
+    auto chunk_of = [&](const int* pre, int j) -> int {
+        int lo = 0, hi = nch;  // pre[lo] <= j < pre[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= j) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
+    // i-th candidate of the threshold bin, in chunk order
+    auto cand_global = [&](int i) -> int2 {
+        const int c = chunk_of(pre_eq, i);
+        return rbase[c * CHUNK + (pre_gt[c + 1] - pre_gt[c]) + (i - pre_eq[c])];
+    };
 
-    int remaining = k - above;
+    // slots above the threshold bin: output columns [0, total_gt) in chunk order
+    for (int j = t; j < total_gt; j += NT) {
+        const int c = chunk_of(pre_gt, j);
+        const int2 e = rbase[c * CHUNK + (j - pre_gt[c])];
+        orow[j] = emit(e.y, wstart);
+        if (osc) osc[j] = key_to_f32((uint32_t)e.x);
+    }
+    const bool in_lds = n_cand <= kResolveCap;
+    if (in_lds)
+        for (int i = t; i < n_cand; i += NT) lcand[i] = cand_global(i);
+    __syncthreads();
+    auto cand_at = [&](int i) -> int2 { return in_lds ? lcand[i] : cand_global(i); };
+
+    int remaining = k - total_gt;
     uint32_t prefix = d1 << 20, pmask = 0xFFF00000u;
     if (remaining < n_cand) {
         const int shifts[2] = {8, 0};
@@ -541,14 +630,14 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
         for (int pass = 0; pass < 2; ++pass) {
             const int nb = 1 << bits[pass];
             const int sh = shifts[pass];
-            for (int i = t; i < nb; i += kChunkThreads) hist[i] = 0;
+            for (int i = t; i < nb; i += NT) hist[i] = 0;
             __syncthreads();
-            for (int i = t; i < n_cand; i += kChunkThreads) {
+            for (int i = t; i < n_cand; i += NT) {
                 const uint32_t key = (uint32_t)cand_at(i).x;
                 if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1);
             }
             __syncthreads();
-            find_bucket<kChunkThreads>(hist, nb, remaining, wave_tot, &sh_digit, &sh_above);
+            find_bucket<NT>(hist, nb, remaining, wave_tot, &sh_digit, &sh_above);
             const int d = sh_digit;
             remaining -= sh_above;
             prefix |= (uint32_t)d << sh;
@@ -558,37 +647,47 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
             if (exact) break;
         }
     }
-    if (t == 0) {
-        cnt_gt = 0;
-        cnt_eq = 0;
-    }
-    __syncthreads();
     const int n_gt = k - remaining;  // slots already placed or strictly above the final threshold
-    for (int i = t; i < n_cand; i += kChunkThreads) {
-        const int2 ck = cand_at(i);
+    int cg = 0, ce = 0, parity = 0;
+    for (int i0 = 0; i0 < n_cand; i0 += NT) {  // uniform trip count
+        const int i = i0 + t;
+        int2 ck = make_int2(0, 0);
+        if (i < n_cand) ck = cand_at(i);
         const uint32_t km = (uint32_t)ck.x & pmask;
+        const bool gt = i < n_cand && km > prefix;
+        const bool eq = i < n_cand && km == prefix;
+        int rg, re, tg, te;
+        round_ranks<NT>(gt, eq, wcnt, parity, &rg, &re, &tg, &te);
         int pos = -1;
-        if (km > prefix) {
-            pos = above + atomicAdd(&cnt_gt, 1);
-        } else if (km == prefix) {
-            const int tk = atomicAdd(&cnt_eq, 1);
+        if (gt) {
+            pos = total_gt + cg + rg;
+        } else if (eq) {
+            const int tk = ce + re;
             if (tk < remaining) pos = n_gt + tk;
         }
         if (pos >= 0) {
             orow[pos] = emit(ck.y, wstart);
-            if (osc) osc[pos] = row[ck.y];
+            if (osc) osc[pos] = key_to_f32((uint32_t)ck.x);
         }
+        cg += tg;
+        ce += te;
+        parity ^= 1;
     }
 }
 
 bool use_chunked(int32_t M, int32_t S_max) { return S_max > kChunk && M < 1024; }
+
+// chunked-path workspace: row headers (zeroed before each call), per-chunk
+// counts (sized for the smaller chunk), candidate regions (one slot each)
+size_t count_words(int32_t S_max) { return (size_t)(S_max + kChunkSmall - 1) / kChunkSmall; }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t M, int32_t S_max)
 {
     if (!use_chunked(M, S_max)) return 0;
-    return (size_t)M * kHeaderWords * sizeof(uint32_t) + (size_t)M * S_max * sizeof(int2);
+    return (size_t)M * kHeaderWords * sizeof(uint32_t) + (size_t)M * count_words(S_max) * sizeof(int2) +
+           (size_t)M * S_max * sizeof(int2);
 }
 
 size_t topk_header_words(int32_t M, int32_t S_max) { return use_chunked(M, S_max) ? (size_t)M * kHeaderWords : 0; }
@@ -607,23 +706,27 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
         return hipGetLastError();
     }
     uint32_t* ghist = static_cast<uint32_t*>(workspace);
-    int2* cand = reinterpret_cast<int2*>(ghist + (size_t)M * kHeaderWords);
+    const int n_counts = (int)count_words(S_max);
+    int2* counts = reinterpret_cast<int2*>(ghist + (size_t)M * kHeaderWords);
+    int2* cand = counts + (size_t)M * n_counts;
     const int n_words = M * kHeaderWords;
     if (!header_zeroed) topk_clear_kernel<<<(n_words + 255) / 256, 256, 0, stream>>>(ghist, n_words);
     // chunk size: 4096 slots, or 2048 when that would leave the chip short of workgroups
     if ((long long)M * ((S_max + kChunk - 1) / kChunk) < kSmallGridWgs) {
         const dim3 grid((S_max + kChunkSmall - 1) / kChunkSmall, M);
         topk_hist_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
-        topk_filter_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
-                                                                            ghist, cand, out_idx, out_scores);
+        topk_filter_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(
+            scores, S_max, positions, valid_len, k, window, ghist, counts, n_counts, cand, out_idx, out_scores);
+        topk_resolve_kernel<kChunkSmall><<<M, kChunkThreads, 0, stream>>>(
+            scores, S_max, positions, valid_len, k, window, ghist, counts, n_counts, cand, out_idx, out_scores);
     } else {
         const dim3 grid((S_max + kChunk - 1) / kChunk, M);
         topk_hist_kernel<kChunk><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
-        topk_filter_kernel<kChunk><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
-                                                                       ghist, cand, out_idx, out_scores);
+        topk_filter_kernel<kChunk><<<grid, kChunkThreads, 0, stream>>>(
+            scores, S_max, positions, valid_len, k, window, ghist, counts, n_counts, cand, out_idx, out_scores);
+        topk_resolve_kernel<kChunk><<<M, kChunkThreads, 0, stream>>>(
+            scores, S_max, positions, valid_len, k, window, ghist, counts, n_counts, cand, out_idx, out_scores);
     }
-    topk_resolve_kernel<<<M, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window, ghist, cand,
-                                                         out_idx, out_scores);
     return hipGetLastError();
 }
 

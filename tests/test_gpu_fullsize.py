@@ -86,15 +86,37 @@ def test_fullsize_fp8_long_decode(dsa):
     _decode_indexer(dsa, w, range(w.M))
 
 
+def _prefill_sample_rows(S, seed=73):
+    """Rows of the 8192-row prefill checked against the oracle.
+
+    The folded scorer gives a workgroup 16-row tile a and its partner tile n - 1 - a; inside a
+    tile, row i sits in lane group (i % 8) / 4 of accumulator register i / 8 (hi) or i / 8 + 2 (lo);
+    key tiles are 32 slots wide, so the causal limit of row r crosses a key-tile edge at r = 32 m - 1.
+    The sample holds the first and last two tiles, the middle pair, every row position inside a
+    tile for pairs drawn across the sequence (with the partner row taken at another position),
+    and rows on both sides of 16- and 32-row edges."""
+    nt = S // 16
+    g = np.random.default_rng(seed)
+    rows = set(range(0, 32)) | set(range(S - 32, S)) | set(range(16 * (nt // 2 - 1), 16 * (nt // 2 + 1)))
+    tiles = g.choice(np.arange(2, nt // 2 - 1), size=64, replace=False)
+    for j, a in enumerate(tiles):
+        rows.add(16 * int(a) + j % 16)                  # every in-tile position, over the drawn tiles
+        rows.add(16 * (nt - 1 - int(a)) + (j + 5) % 16)  # the partner tile, at another position
+    for m in g.choice(np.arange(1, S // 32), size=24, replace=False):
+        rows.update((32 * int(m) - 1, 32 * int(m), 32 * int(m) + 16))
+    return np.array(sorted(r for r in rows if 0 <= r < S))
+
+
 def test_fullsize_prefill(dsa):
     w = synthetic.make_workload("prefill")
     S = w.S_max
-    announce("prefill full: 8192 queries x 8192 keys causal, 64 heads, top-2048 (sampled rows)")
+    announce("prefill full: 8192 queries x 8192 keys causal, 64 heads, top-2048 (>= 256 sampled rows)")
     scores = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
                                  positions=_cuda(w.positions), rows_per_seq=w.rows_per_seq)
     idx = dsa.dsa_topk(scores, w.index_topk, positions=_cuda(w.positions))
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 7, 8, 31, 32, 33, 1000, 2046, 2047, 2048, 4095, 4096, 6000, 8190, 8191])
+    rows = _prefill_sample_rows(S)
+    assert len(rows) >= 256
     sc = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
     # all 8192 rows share one cache: the oracle rows map to it with rows_per_seq = len(rows)
     ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache, scale=w.index_scale,
