@@ -51,6 +51,9 @@ def parse():
                     choices=["full_decode_step", "tiny_decode", "batched_decode", "fp8_long_decode", "prefill",
                              "cache_write", "prefill_attn"])
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--configs", choices=["on", "off"], default="on",
+                    help="full_decode_step: also measure the other four configurations (scorer and top-k legs "
+                         "of the batched and long fp8 decode indexers and of the prefill scorer, the tiny step)")
     ap.add_argument("--indexer-relu", action="store_true",
                     help="indexer activation max(0, .) per head (per-head MFMA scorer) instead of the identity")
     ap.add_argument("--paged", type=int, default=0, metavar="PAGE",
@@ -97,6 +100,215 @@ def event_time_ms(torch, fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def graph_time_ms(torch, fn, reps, replays=3, outputs=()):
+    """Device time per fn() call: `reps` calls captured in one HIP graph and replayed `replays` times
+    between two events, so no host-side launch cost is inside the measurement.  fn must neither allocate
+    nor synchronise, and a call sequence of `reps` calls must end where it started (rotations cycle
+    completely).  The tensors in `outputs` must hold the same bytes after the replays as after `reps`
+    eager calls (every kernel here is deterministic), which checks the captured work."""
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = event_time_ms(torch, g.replay, replays) / reps
+    for a, b in zip(ref, outputs):
+        if not torch.equal(a.view(torch.uint8), b.contiguous().view(torch.uint8)):
+            raise RuntimeError("a graph replay gave other results than the eager call")
+    del g
+    return ms
+
+
+def rotation_count(args, set_bytes):
+    """Copies of the inputs and outputs to cycle over so that each timed call streams from HBM: enough
+    for twice the 256 MB Infinity Cache and at least 4 when one set is smaller than that."""
+    if args.rotate > 0:
+        return args.rotate
+    return max(4, -(-2 * MALL_BYTES // set_bytes)) if set_bytes < 2 * MALL_BYTES else 1
+
+
+def host_threads():
+    import oracle
+
+    return oracle.default_threads()
+
+
+def upload(torch, w, dev):
+    c = lambda t: None if t is None else t.contiguous().to(dev)  # noqa: E731
+    return c(w.index_q), c(w.index_w), c(w.k_cache), c(w.k_scale), c(w.positions)
+
+
+def score_bytes_of(w, nv):
+    B, H, D = w.index_q.shape
+    per_slot = D * (1 if w.key_fp8 else 2) + (4 if w.key_fp8 else 0)
+    return int(nv.sum()) * per_slot + B * w.S_max * 4 + B * H * D * 2 + B * H * 4
+
+
+def indexer_legs(args, torch, dsa, w, dev, relu=False, paging=None, s_max=None):
+    """Scorer and top-k of a decode indexer workload, each timed from replayed HIP graphs over rotated
+    input sets with every output and workspace allocated beforehand.  Returns the timings and the first
+    set's scores and top-k rows."""
+    B = w.M
+    S_max = w.S_max
+    k = w.index_topk
+    pkw = {"paging": paging, "s_max": s_max} if paging is not None else {}
+    base = upload(torch, w, dev)
+    if paging is not None:
+        base = (base[0], base[1], args._pool_k, args._pool_ks, base[4])
+    scores = torch.empty((B, S_max), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    nws = dsa.topk_workspace_bytes(B, S_max, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in base + (scores, idx) if t is not None)
+    n_rot = 1 if paging is not None else rotation_count(args, set_bytes)
+    sets = [base + (scores, idx)]
+    for _ in range(n_rot - 1):
+        sets.append(tuple(None if t is None else t.clone() for t in sets[0]))
+    torch.cuda.synchronize()
+    rot = [0]
+
+    def nxt():
+        i = rot[0]
+        rot[0] = (i + 1) % n_rot
+        return sets[i]
+
+    def score_once():
+        q_, w_, k_, ks_, pos_, sc_, _ = nxt()
+        dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, k_scale=ks_, positions=pos_, valid_len=w.valid_len,
+                            relu=relu, out=sc_, **pkw)
+
+    def topk_once():
+        _, _, _, _, pos_, sc_, id_ = nxt()
+        dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len, out=id_, workspace=ws)
+
+    reps = max(args.steps, n_rot)
+    reps -= reps % n_rot
+    ms_score = graph_time_ms(torch, score_once, reps, outputs=[s[5] for s in sets])
+    rot[0] = 0
+    ms_topk = graph_time_ms(torch, topk_once, reps, outputs=[s[6] for s in sets])
+    return ms_score, ms_topk, n_rot, scores, idx
+
+
+def indexer_entry(w, nv, ms_score, ms_topk, n_rot):
+    sb = score_bytes_of(w, nv)
+    n_slots = int(nv.sum())
+    tb = n_slots * 4 + w.M * w.index_topk * 4
+    return {"score_us": ms_score * 1e3, "score_GB/s": sb / ms_score / 1e6,
+            "score_hbm_frac": sb / ms_score / 1e6 / HBM_PEAK_GBS, "score_bytes": sb,
+            "key_slots_per_s": n_slots / ms_score * 1e3, "topk_us": ms_topk * 1e3, "topk_bytes": tb,
+            "input_sets": n_rot}
+
+
+def config_indexer(args, torch, dsa, synthetic, dev, name, number):
+    """Configs 2 and 4 (decode indexer only): scorer and top-k legs with rotation, parity on sampled rows."""
+    import oracle
+    from parity import check_scores, check_topk_own_scores, n_valid_rows
+
+    w = synthetic.make_workload(name)
+    nv = w.n_valid().numpy()
+    ms_s, ms_t, n_rot, scores, idx = indexer_legs(args, torch, dsa, w, dev)
+    e = {"config": number, **indexer_entry(w, nv, ms_s, ms_t, n_rot)}
+    rows = np.array([0, w.M - 1])
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache[rows],
+                             k_scale=None if w.k_scale is None else w.k_scale[rows], scale=w.index_scale,
+                             positions=w.positions[rows], valid_len=w.valid_len)
+    check_scores(scores.cpu().numpy()[rows], ref, nv[rows], oracle.mask_bound())
+    check_topk_own_scores(idx.cpu().numpy()[rows], ref, nv[rows], w.index_topk)
+    e["parity"] = "ok (rows %s)" % rows.tolist()
+    log("config %d %s: score %.1f us (%.1f%% HBM), top-k %.1f us, %d input sets" % (
+        number, name, e["score_us"], 100 * e["score_hbm_frac"], e["topk_us"], n_rot))
+    return e
+
+
+def config_prefill(args, torch, dsa, synthetic, dev):
+    """Config 3: the prefill scorer (identity: heads folded, HBM-bound on the score writes; ReLU: per-head
+    MFMA) and the prefill top-k, with rotation, parity on sampled rows."""
+    import oracle
+    from parity import check_scores, check_topk_own_scores
+
+    w = synthetic.make_workload("prefill")
+    S, H, D = w.index_q.shape
+    gq, gw, gk, _, gpos = upload(torch, w, dev)
+    scores = torch.empty((S, S), dtype=torch.float32, device=dev)
+    idx = torch.empty((S, w.index_topk), dtype=torch.int32, device=dev)
+    set_bytes = sum(t.numel() * t.element_size() for t in (gq, gw, gk, gpos, scores, idx))
+    n_rot = rotation_count(args, set_bytes)
+    sets = [(gq, gw, gk, gpos, scores, idx)] + [
+        tuple(t.clone() for t in (gq, gw, gk, gpos, scores, idx)) for _ in range(n_rot - 1)]
+    torch.cuda.synchronize()
+    rot = [0]
+
+    def nxt():
+        i = rot[0]
+        rot[0] = (i + 1) % n_rot
+        return sets[i]
+
+    def score(relu):
+        def f():
+            q_, w_, k_, p_, sc_, _ = nxt()
+            dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, positions=p_, rows_per_seq=S, relu=relu, out=sc_)
+        return f
+
+    def topk_once():
+        _, _, _, p_, sc_, id_ = nxt()
+        dsa.dsa_topk(sc_, w.index_topk, positions=p_, out=id_)
+
+    reps = n_rot * max(1, args.steps // (2 * n_rot))
+    pairs = S * (S + 1) // 2
+    flops = 2.0 * H * D * pairs
+    nbytes = S * S * 4 + S * H * D * 2 + S * H * 4 + S * D * 2
+    ms_relu = graph_time_ms(torch, score(True), reps, outputs=[s[4] for s in sets])
+    rot[0] = 0
+    ms_fold = graph_time_ms(torch, score(False), reps, outputs=[s[4] for s in sets])
+    rot[0] = 0
+    ms_topk = graph_time_ms(torch, topk_once, reps, outputs=[s[5] for s in sets])
+    rows = np.array([0, 31, 2047, 4096, 6001, S - 1])
+    sc = scores[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache, scale=w.index_scale,
+                             positions=w.positions[rows], rows_per_seq=len(rows))
+    check_scores(sc, ref, rows + 1, oracle.mask_bound())
+    check_topk_own_scores(idx.cpu().numpy()[rows], ref, rows + 1, w.index_topk)
+    e = {"config": 3, "score_fold_us": ms_fold * 1e3, "score_fold_GB/s": nbytes / ms_fold / 1e6,
+         "score_fold_hbm_frac": nbytes / ms_fold / 1e6 / HBM_PEAK_GBS, "score_fold_bytes": nbytes,
+         "score_relu_us": ms_relu * 1e3, "score_relu_TFLOP/s": flops / ms_relu / 1e9,
+         "score_relu_mfma_frac": flops / ms_relu / 1e9 / MFMA_BF16_PEAK_TFLOPS, "per_head_flops": flops,
+         "topk_us": ms_topk * 1e3, "input_sets": n_rot, "parity": "ok (identity scores, rows %s)" % rows.tolist()}
+    log("config 3 prefill: fold score %.1f us (%.1f%% HBM), ReLU score %.1f us (%.1f%% MFMA), top-k %.1f us" % (
+        e["score_fold_us"], 100 * e["score_fold_hbm_frac"], e["score_relu_us"], 100 * e["score_relu_mfma_frac"],
+        e["topk_us"]))
+    return e
+
+
+def config_tiny(args, torch, dsa, synthetic, dev):
+    """Config 1: the tiny decode step, timed from a replayed graph, checked whole against the oracle."""
+    import oracle
+    from parity import check_attn, check_index_list, check_scores, n_valid_rows
+
+    w = synthetic.make_workload("tiny_decode")
+    gq, gw, gk, _, _ = upload(torch, w, dev)
+    c = lambda t: t.contiguous().to(dev)  # noqa: E731
+    step = dsa.DecodeStep(gq, gw, gk, valid_len=w.valid_len, index_scale=w.index_scale, index_topk=w.index_topk,
+                          window=w.window, q=c(w.q), kv=c(w.kv), attn_sink=c(w.sink), sm_scale=w.sm_scale, dv=w.dv)
+    ms = graph_time_ms(torch, step, 50, outputs=[step.out, step.index_list])
+    nv = n_valid_rows(None, w.valid_len, 1, w.S_max)
+    ref_sc = oracle.index_score(w.index_q, w.index_w, w.k_cache, scale=w.index_scale, valid_len=w.valid_len)
+    check_scores(step.scores.cpu().numpy(), ref_sc, nv, oracle.mask_bound())
+    ref_top = oracle.topk(ref_sc, w.index_topk, valid_len=w.valid_len)
+    ref_list = oracle.assemble(ref_top, s_max=w.S_max, window=w.window, valid_len=w.valid_len)
+    check_index_list(step.index_list.cpu().numpy(), ref_list, ref_sc, nv, w.index_topk, w.window)
+    ref_out, _ = oracle.sparse_attn(w.q, w.kv, w.sink, step.index_list.cpu().numpy()[:, None, :],
+                                    sm_scale=w.sm_scale, dv=w.dv)
+    err, rel = check_attn(step.out.float().cpu().numpy(), ref_out)
+    log("config 1 tiny_decode: step %.1f us" % (ms * 1e3))
+    return {"config": 1, "step_us": ms * 1e3, "parity": "ok (whole step; attention max abs %.2g, rel-L2 %.2g)" % (
+        err, rel)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -110,6 +322,7 @@ def main():
     import sparse_attention_amd as dsa
     import synthetic
 
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
     dsa.load_library()
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -123,10 +336,10 @@ def main():
         return bench_prefill_attn(args, torch, dsa, synthetic, dev)
     w = synthetic.make_workload(args.workload)
     log("generated %s in %.1fs" % (args.workload, time.time() - t0))
-    c = lambda t: None if t is None else t.contiguous().to(dev)  # noqa: E731
-    gq, gw, gk, gks, gpos = c(w.index_q), c(w.index_w), c(w.k_cache), c(w.k_scale), c(w.positions)
+    gq, gw, gk, gks, gpos = upload(torch, w, dev)
     has_attn = w.q is not None
     if has_attn:
+        c = lambda t: t.contiguous().to(dev)  # noqa: E731
         gaq, gkv, gsink = c(w.q), c(w.kv), c(w.sink)
     torch.cuda.synchronize()
     log("inputs resident on %s" % torch.cuda.get_device_name(0))
@@ -135,8 +348,6 @@ def main():
     S_max = w.S_max
     nv = w.n_valid().numpy()
     n_slots = int(nv.sum())
-    key_bytes_per_slot = D * (1 if w.key_fp8 else 2) + (4 if w.key_fp8 else 0)
-    score_bytes = n_slots * key_bytes_per_slot + B * S_max * 4 + B * H * D * 2 + B * H * 4
     k = w.index_topk
     K_top = k + w.window
 
@@ -162,26 +373,29 @@ def main():
             return pool
 
         gk, gks = to_pool(gk), to_pool(gks)
+        args._pool_k, args._pool_ks = gk, gks
         if has_attn:
             gkv = to_pool(gkv)
         torch.cuda.synchronize()
         paging = dsa.Paging(table.to(dev), P, n_pages)
         pkw = {"paging": paging}
         log("page pools: %d pages of %d slots" % (n_pages, P))
+
+    # ---- the step (the headline number): eager calls between two events
     if has_attn:
         step = dsa.DecodeStep(gq, gw, gk, k_scale=gks, positions=gpos, valid_len=w.valid_len,
                               index_scale=w.index_scale, index_topk=k, window=w.window, q=gaq, kv=gkv,
                               attn_sink=gsink, sm_scale=w.sm_scale, dv=w.dv, relu=args.indexer_relu,
                               s_max=S_max if paging else None, **pkw)
         run_step = step
+        n_rot = 1
     else:
         scores_buf = torch.empty((B, S_max), dtype=torch.float32, device=dev)
-        # Indexer-only workloads fit in the 256 MB Infinity Cache: cycle over
-        # copies of every input and output at distinct addresses so that each
-        # timed call streams from HBM (footprint >= 2 x the cache).
+        idx_buf = torch.empty((B, k), dtype=torch.int32, device=dev)
+        nws = dsa.topk_workspace_bytes(B, S_max, k)
+        ws_buf = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         set_bytes = sum(t.numel() * t.element_size() for t in (gq, gw, gk, gks, gpos, scores_buf) if t is not None)
-        n_rot = args.rotate if args.rotate > 0 else (
-            max(4, -(-2 * MALL_BYTES // set_bytes)) if set_bytes < 2 * MALL_BYTES else 1)
+        n_rot = 1 if paging else rotation_count(args, set_bytes)
         sets = [(gq, gw, gk, gks, gpos, scores_buf)]
         for _ in range(n_rot - 1):
             sets.append(tuple(None if t is None else t.clone() for t in sets[0]))
@@ -191,17 +405,14 @@ def main():
                                                                           n_rot * set_bytes / 1e6))
         rot = [0]
 
-        def next_set():
+        def run_step():
             i = rot[0]
             rot[0] = (i + 1) % n_rot
-            return sets[i]
-
-        def run_step():
-            q_, w_, k_, ks_, pos_, sc_ = next_set()
+            q_, w_, k_, ks_, pos_, sc_ = sets[i]
             dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, k_scale=ks_, positions=pos_,
                                 valid_len=w.valid_len, relu=args.indexer_relu, out=sc_,
                                 s_max=S_max if paging else None, **pkw)
-            return dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len)
+            dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len, out=idx_buf, workspace=ws_buf)
 
     for _ in range(args.warmup):
         run_step()
@@ -211,45 +422,31 @@ def main():
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
     log("step %.3f ms (host wall %.3f ms/step)" % (ms_step, wall_ms))
 
-    # per-kernel timings (same inputs, same stream; the same rotation)
-    scores_t = step.scores if has_attn else scores_buf
-    if has_attn:
-        n_rot = 1
-        sets = [(gq, gw, gk, gks, gpos, scores_t)]
-        rot = [0]
-
-        def next_set():
-            return sets[0]
-    kern = {}
-
-    def score_once():
-        q_, w_, k_, ks_, pos_, sc_ = next_set()
-        dsa.dsa_index_score(q_, w_, k_, scale=w.index_scale, k_scale=ks_, positions=pos_, valid_len=w.valid_len,
-                            relu=args.indexer_relu, out=sc_, s_max=S_max if paging else None, **pkw)
-
-    def topk_once():
-        q_, w_, k_, ks_, pos_, sc_ = next_set()
-        dsa.dsa_topk(sc_, k, positions=pos_, valid_len=w.valid_len)
-
-    ms_score = event_time_ms(torch, score_once, args.steps)
+    # ---- per-kernel legs: replayed HIP graphs, every output and workspace allocated beforehand
+    ms_score, ms_topk, n_rot_legs, scores_leg, _ = indexer_legs(
+        args, torch, dsa, w, dev, relu=args.indexer_relu, paging=paging, s_max=S_max if paging else None)
     score_name = "score_decode_relu" if args.indexer_relu else "score_decode"
-    kern[score_name] = {"us": ms_score * 1e3, "bytes": score_bytes,
-                            "GB/s": score_bytes / ms_score / 1e6,
-                            "hbm_frac": score_bytes / ms_score / 1e6 / HBM_PEAK_GBS,
-                            "key_slots_per_s": n_slots / ms_score * 1e3}
-    ms_topk = event_time_ms(torch, topk_once, args.steps)
-    topk_bytes = n_slots * 4 + B * k * 4
-    kern["topk"] = {"us": ms_topk * 1e3, "bytes": topk_bytes, "GB/s": topk_bytes / ms_topk / 1e6}
-    step_bytes = score_bytes + topk_bytes
+    e = indexer_entry(w, nv, ms_score, ms_topk, n_rot_legs)
+    kern = {score_name: {"us": e["score_us"], "bytes": e["score_bytes"], "GB/s": e["score_GB/s"],
+                         "hbm_frac": e["score_hbm_frac"], "key_slots_per_s": e["key_slots_per_s"]},
+            "topk": {"us": e["topk_us"], "bytes": e["topk_bytes"], "GB/s": e["topk_bytes"] / ms_topk / 1e6,
+                     "note": "standalone dsa_topk, including its header-clear launch (in the step the scorer "
+                             "clears the header)"}}
+    step_bytes = e["score_bytes"] + e["topk_bytes"]
     if has_attn:
         lst = step.index_list.view(B, 1, K_top)
         n_entries = int((step.index_list >= 0).sum().item())
         Hq, Dqk, Dv = w.q.shape[2], w.q.shape[3], w.dv
         attn_bytes = n_entries * Dqk * 2 + B * Hq * Dqk * 2 + B * Hq * Dv * 2 + B * K_top * 4
         attn_flops = 2.0 * Hq * n_entries * (Dqk + Dv)
-        ms_attn = event_time_ms(torch, lambda: dsa.dsa_sparse_attn(gaq, gkv, gsink, lst, sm_scale=w.sm_scale,
-                                                                  dv=Dv, s_kv=S_max if paging else None, **pkw),
-                                args.steps)
+        attn_out = torch.empty((B, 1, Hq, Dv), dtype=torch.bfloat16, device=dev)
+        nws_a = dsa.sparse_attn_workspace_bytes(B, 1, Hq, Dv, K_top)
+        ws_a = torch.empty(max(nws_a, 1), dtype=torch.uint8, device=dev)
+        ms_attn = graph_time_ms(torch, lambda: dsa.dsa_sparse_attn(
+            gaq, gkv, gsink, lst, sm_scale=w.sm_scale, dv=Dv, out=attn_out, workspace=ws_a,
+            s_kv=S_max if paging else None, **pkw), args.steps, outputs=[attn_out])
+        if not torch.equal(attn_out, step.out):
+            raise RuntimeError("the attention leg differs from the step's attention on the same list")
         kern["sparse_attn"] = {"us": ms_attn * 1e3, "bytes": attn_bytes, "flops": attn_flops,
                                "GB/s": attn_bytes / ms_attn / 1e6,
                                "hbm_frac": attn_bytes / ms_attn / 1e6 / HBM_PEAK_GBS,
@@ -257,13 +454,15 @@ def main():
                                "tokens_per_s": B / ms_attn * 1e3,
                                "kv_entries_per_s": n_entries / ms_attn * 1e3}
         step_bytes += attn_bytes
+        ms_step_graph = graph_time_ms(torch, step, max(4, args.steps // 2), outputs=[step.out, step.index_list])
+        log("step from a replayed graph %.3f ms" % ms_step_graph)
     for name, v in kern.items():
         log("%-12s %9.2f us  %8.1f GB/s" % (name, v["us"], v["GB/s"]))
 
     if args.copy_calibration:
         copy_calibration(torch, dev)
 
-    # dominant kernel roofline (HBM-bound streaming scorer)
+    # ---- dominant kernel roofline (HBM-bound streaming scorer)
     dom = max(kern, key=lambda n: kern[n]["us"])
     traffic = None
     if os.path.exists(PMC_FILE):
@@ -281,11 +480,31 @@ def main():
     roof["traffic"] = traffic
     roof["kernel"] = dom
 
-    # CPU oracle on a bounded sample of the same workload (+ parity on the timed buffers)
+    # ---- the other configurations, measured in this run (default workload only)
+    configs = None
+    if args.workload == "full_decode_step" and args.configs == "on" and not args.paged and not args.indexer_relu:
+        configs = {"full_decode_step": {
+            "config": 5, "step_us": ms_step * 1e3, "step_graph_us": ms_step_graph * 1e3,
+            "step_hbm_frac": step_bytes / ms_step / 1e6 / HBM_PEAK_GBS, "score_us": kern[score_name]["us"],
+            "score_hbm_frac": kern[score_name]["hbm_frac"], "topk_us": kern["topk"]["us"],
+            "attn_us": kern["sparse_attn"]["us"], "attn_hbm_frac": kern["sparse_attn"]["hbm_frac"],
+            "attn_mfma_frac": kern["sparse_attn"]["mfma_frac"]}}
+        configs["tiny_decode"] = config_tiny(args, torch, dsa, synthetic, dev)
+        configs["batched_decode"] = config_indexer(args, torch, dsa, synthetic, dev, "batched_decode", 2)
+        torch.cuda.empty_cache()
+        configs["prefill"] = config_prefill(args, torch, dsa, synthetic, dev)
+        torch.cuda.empty_cache()
+        configs["fp8_long_decode"] = config_indexer(args, torch, dsa, synthetic, dev, "fp8_long_decode", 4)
+        torch.cuda.empty_cache()
+
+    # ---- CPU oracle on a bounded sample of the same workload (+ parity on the timed buffers)
     cpu = None
     parity = None
     if args.cpu_baseline == "on":
+        scores_t = step.scores if has_attn else scores_leg
         cpu, parity = cpu_baseline(args, w, step if has_attn else None, scores_t, nv, torch)
+        if args.workload == "full_decode_step" and not args.paged and not args.indexer_relu:
+            cpu["single_thread"] = single_thread_rates(args, synthetic)
 
     rec = {
         "metric": METRIC,
@@ -316,6 +535,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
+        "configs": configs,
     }
     print(json.dumps(rec), flush=True)
 
@@ -504,6 +724,58 @@ def bench_cache_write(args, torch, dsa, synthetic, dev):
     print(json.dumps(rec), flush=True)
 
 
+def single_thread_rates(args, synthetic):
+    """The oracle on one thread for configs 1, 2 and 4: the whole tiny step, and score + top-k of one
+    sequence of the batched and the long fp8 decode, each repeated for about two seconds."""
+    import oracle
+
+    out = {}
+    budget = min(2.0, args.cpu_seconds)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                return n, time.perf_counter() - t0
+
+    w = synthetic.make_workload("tiny_decode")
+    nv = int(w.n_valid().sum())
+
+    def tiny():
+        sc = oracle.index_score(w.index_q, w.index_w, w.k_cache, scale=w.index_scale, valid_len=w.valid_len,
+                                nthreads=1)
+        top = oracle.topk(sc, w.index_topk, valid_len=w.valid_len, nthreads=1)
+        lst = oracle.assemble(top, s_max=w.S_max, window=w.window, valid_len=w.valid_len)
+        oracle.sparse_attn(w.q, w.kv, w.sink, lst[:, None, :], sm_scale=w.sm_scale, dv=w.dv, nthreads=1)
+
+    n, sec = timed(tiny)
+    out["tiny_decode"] = {"config": 1, "value": n * nv / sec, "unit": "key-slots/s", "steps_per_s": n / sec,
+                          "sample": "%d whole step(s): score + full-sort top-k + attention" % n}
+    for name, number in (("batched_decode", 2), ("fp8_long_decode", 4)):
+        w = synthetic.make_workload(name)
+        r = slice(0, 1)
+        nv0 = int(w.n_valid()[0])
+
+        def one(w=w, r=r):
+            sc = oracle.index_score(w.index_q[r], w.index_w[r], w.k_cache[r],
+                                    k_scale=None if w.k_scale is None else w.k_scale[r], scale=w.index_scale,
+                                    positions=w.positions[r], valid_len=w.valid_len, nthreads=1)
+            oracle.topk(sc, w.index_topk, positions=w.positions[r], valid_len=w.valid_len, nthreads=1)
+
+        n, sec = timed(one)
+        out[name] = {"config": number, "value": n * nv0 / sec, "unit": "key-slots/s",
+                     "sample": "%d pass(es) of score + full-sort top-k over sequence 0 (%d attendable slots)" % (
+                         n, nv0)}
+        del w
+    for v in out.values():
+        v["cores"] = 1
+    log("oracle on one thread: " + ", ".join("%s %.3g key-slots/s" % (k, v["value"]) for k, v in out.items()))
+    return out
+
+
 def cpu_baseline(args, w, step, scores_t, nv, torch):
     """Time the oracle (as it stands) on `cpu_sample` sequences of the same workload, and check the
     GPU's outputs for those sequences against it."""
@@ -514,8 +786,7 @@ def cpu_baseline(args, w, step, scores_t, nv, torch):
 
     ns = min(args.cpu_sample, w.M)
     rows = np.linspace(0, w.M - 1, ns).round().astype(np.int64)
-    threads = oracle.default_threads()
-    threads = min(threads, 16)
+    threads = oracle.default_threads()  # every core in the affinity mask, or OMP_NUM_THREADS if set lower
     whole = ns == w.M  # the sample is the whole batch: no copies
     sub = lambda t: None if t is None else (t if whole else t[rows])  # noqa: E731
     pos = sub(w.positions)

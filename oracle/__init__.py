@@ -69,10 +69,16 @@ def _load():
 
 
 def default_threads() -> int:
+    """Every core this process may run on, or OMP_NUM_THREADS when that is set lower (a host that grants
+    the process a share of its cores says so there)."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and 0 < int(env) < n:
+        n = int(env)
+    return n
 
 
 def _raw(x):

@@ -197,29 +197,45 @@ def dsa_index_score(q, w, k_cache, *, scale: float, k_scale=None, positions=None
     return out
 
 
-def dsa_topk(scores, index_topk: int, *, positions=None, valid_len: int = -1, with_scores: bool = False):
-    """Top-k slot indices [M, index_topk] int32 (unordered set per row, -1 padded)."""
+def topk_workspace_bytes(M: int, S_max: int, index_topk: int) -> int:
+    return int(load_library().dsa_topk_workspace_size(int(M), int(S_max), int(index_topk)))
+
+
+def dsa_topk(scores, index_topk: int, *, positions=None, valid_len: int = -1, with_scores: bool = False,
+             out=None, workspace=None):
+    """Top-k slot indices [M, index_topk] int32 (unordered set per row, -1 padded; the same scores give
+    the same row on every call).  ``out`` and ``workspace`` (uint8, at least topk_workspace_bytes) may be
+    given to avoid allocations."""
     _dev(scores, "scores", (torch.float32,))
     if positions is not None:
         _dev(positions, "positions", (torch.int32,))
     M, S_max = scores.shape
     lib = load_library()
-    idx = torch.empty((M, index_topk), dtype=torch.int32, device=scores.device)
+    idx = out if out is not None else torch.empty((M, index_topk), dtype=torch.int32, device=scores.device)
+    _dev(idx, "out", (torch.int32,))
+    if tuple(idx.shape) != (M, index_topk):
+        raise ValueError("out must be [M, index_topk]")
     tsc = torch.empty((M, index_topk), dtype=torch.float32, device=scores.device) if with_scores else None
     nws = lib.dsa_topk_workspace_size(M, S_max, int(index_topk))
-    ws = _workspace(nws, scores.device)
+    ws = workspace if workspace is not None else _workspace(nws, scores.device)
+    if nws and (ws is None or ws.numel() * ws.element_size() < nws):
+        raise ValueError("workspace must hold %d bytes" % nws)
     st = lib.dsa_topk(_ptr(scores), M, S_max, _ptr(positions), int(valid_len), int(index_topk), _ptr(idx), _ptr(tsc),
                       _ptr(ws), nws, _stream())
     _check("dsa_topk", st)
     return (idx, tsc) if with_scores else idx
 
 
+def sparse_attn_workspace_bytes(B: int, S: int, Hq: int, dv: int, K_top: int) -> int:
+    return int(load_library().dsa_sparse_attn_workspace_size(int(B), int(S), int(Hq), int(dv), int(K_top)))
+
+
 def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False, out=None,
-                    paging: Optional[Paging] = None, s_kv: Optional[int] = None):
+                    paging: Optional[Paging] = None, s_kv: Optional[int] = None, workspace=None):
     """Sparse MQA with sink.  q [B, S, Hq, Dqk] bf16; kv [B, S_kv, Dqk] bf16; attn_sink [Hq] fp32 or None;
     topk_idx [B, S, K_top] int32.  Returns out [B, S, Hq, dv] bf16 (and lse [B, S, Hq] fp32); `out` may be
-    given.  With ``paging``, kv is a page pool [n_pages * page_size, Dqk] and ``s_kv`` the logical slot
-    count of every sequence."""
+    given, and so may ``workspace`` (uint8, at least sparse_attn_workspace_bytes).  With ``paging``, kv is a
+    page pool [n_pages * page_size, Dqk] and ``s_kv`` the logical slot count of every sequence."""
     _dev(q, "q", (torch.bfloat16,))
     _dev(kv, "kv", (torch.bfloat16,))
     _dev(topk_idx, "topk_idx", (torch.int32,))
@@ -238,7 +254,9 @@ def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, wit
         raise ValueError("out must be [B, S, Hq, dv]")
     lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device) if with_lse else None
     nws = lib.dsa_sparse_attn_workspace_size(B, S, Hq, int(dv), K_top)
-    ws = _workspace(nws, q.device)
+    ws = workspace if workspace is not None else _workspace(nws, q.device)
+    if nws and (ws is None or ws.numel() * ws.element_size() < nws):
+        raise ValueError("workspace must hold %d bytes" % nws)
     if paging is not None:
         st = lib.dsa_sparse_attn_paged(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idx), ctypes.byref(paging.struct),
                                        B, S, Hq, Dqk, int(dv), S_kv, K_top, float(sm_scale), _ptr(out), _ptr(lse),

@@ -122,6 +122,108 @@ __device__ __forceinline__ float key_to_f32(uint32_t key)
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Deterministic output pass of a row path: wave w of NT / 64 owns the slot
+// range [w * span, (w + 1) * span) (span a multiple of 256), a lane takes 4
+// consecutive slots per step.  Each wave counts its slots above the final
+// threshold (gt) and at it (eq); one barrier shares the counts; then each
+// wave emits its range in slot order: gt slots from column (gt count of the
+// lower waves), eq slots from n_gt + (eq count of the lower waves) while
+// fewer than `remaining` are placed.  key4(s) gives the order keys of slots
+// s .. s + 3 (s a multiple of 4; slots >= nv are never used).
+template <int NT, typename Key4>
+__device__ __forceinline__ void emit_row(Key4 key4, int nv, uint32_t prefix, uint32_t pmask, int k,
+                                         int remaining, int wstart, int (*wcnt)[NT / 64], int32_t* __restrict__ orow,
+                                         float* __restrict__ osc)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int span = ((nv + NT / 64 - 1) / (NT / 64) + 255) & ~255;
+    const int lo = wave * span;
+    const int hi = min(lo + span, nv);
+    int c_gt = 0, c_eq = 0;
+    for (int s0 = lo; s0 < hi; s0 += 256) {  // wave-uniform trip count
+        const int s = s0 + 4 * lane;
+        if (s < hi) {
+            const u32x4 kk = key4(s);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t km = kk[e] & pmask;
+                const bool in = s + e < hi;
+                c_gt += (in && km > prefix) ? 1 : 0;
+                c_eq += (in && km == prefix) ? 1 : 0;
+            }
+        }
+    }
+    c_gt = wave_sum(c_gt);
+    c_eq = wave_sum(c_eq);
+    if (lane == 0) {
+        wcnt[0][wave] = c_gt;
+        wcnt[1][wave] = c_eq;
+    }
+    __syncthreads();
+    int bgt = 0, beq = 0;
+    for (int w = 0; w < wave; ++w) {
+        bgt += wcnt[0][w];
+        beq += wcnt[1][w];
+    }
+    const int n_gt = k - remaining;
+    for (int s0 = lo; s0 < hi; s0 += 256) {
+        const int s = s0 + 4 * lane;
+        u32x4 kk = {0u, 0u, 0u, 0u};
+        int fl = 0;  // bit e: slot s + e is gt; bit 4 + e: eq
+        if (s < hi) {
+            kk = key4(s);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t km = kk[e] & pmask;
+                const bool in = s + e < hi;
+                fl |= (in && km > prefix) ? (1 << e) : 0;
+                fl |= (in && km == prefix) ? (16 << e) : 0;
+            }
+        }
+        const int mine = __popc(fl & 15) | (__popc(fl >> 4) << 16);  // this lane's gt | eq << 16
+        const int incl = wave_inclusive_scan(mine);
+        const int tot = __shfl(incl, 63, 64);
+        int g = bgt + ((incl - mine) & 0xFFFF);
+        int q = beq + ((incl - mine) >> 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            int pos = -1;
+            if (fl & (1 << e)) {
+                pos = g++;
+            } else if (fl & (16 << e)) {
+                if (q < remaining) pos = n_gt + q;
+                ++q;
+            }
+            if (pos >= 0) {
+                orow[pos] = emit(s + e, wstart);
+                if (osc) osc[pos] = key_to_f32(kk[e]);
+            }
+        }
+        bgt += tot & 0xFFFF;
+        beq += tot >> 16;
+    }
+}
+
 // Deterministic compaction of one round of a workgroup of NT threads: this
 // thread's rank among the round's `gt` threads and among its `eq` threads
 // (lower waves first, then lower lanes), and the round's totals.  wcnt is a
@@ -165,7 +267,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 {
     __shared__ int hist[kBins];
     __shared__ int wave_tot[kRowThreads / 64];
-    __shared__ int wcnt[2][2][kRowThreads / 64];
+    __shared__ int wcnt[2][kRowThreads / 64];
     __shared__ int sh_digit, sh_above;
 
     const int r = blockIdx.x;
@@ -214,38 +316,21 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         if (exact) break;
     }
 
-    const int n_gt = k - remaining;
-    int carry_gt = 0, carry_eq = 0, parity = 0;
-    for (int s0 = 0; s0 < nv; s0 += kRowThreads) {  // uniform trip count
-        const int s = s0 + t;
-        const float v = s < nv ? row[s] : 0.f;
-        const uint32_t km = f32_order_key(v) & pmask;
-        const bool gt = s < nv && km > prefix;
-        const bool eq = s < nv && km == prefix;
-        int rg, re, tg, te;
-        round_ranks<kRowThreads>(gt, eq, wcnt, parity, &rg, &re, &tg, &te);
-        int pos = -1;
-        if (gt) {
-            pos = carry_gt + rg;
-        } else if (eq) {
-            const int tk = carry_eq + re;
-            if (tk < remaining) pos = n_gt + tk;
-        }
-        if (pos >= 0) {
-            orow[pos] = emit(s, wstart);
-            if (osc) osc[pos] = v;
-        }
-        carry_gt += tg;
-        carry_eq += te;
-        parity ^= 1;
-    }
+    // (rows of this path may have any length: the four slots are read one by one, those past n_valid not at all)
+    emit_row<kRowThreads>(
+        [&](int s) {
+            u32x4 kk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kk[e] = s + e < nv ? f32_order_key(row[s + e]) : 0u;
+            return kk;
+        },
+        nv, prefix, pmask, k, remaining, wstart, wcnt, orow, osc);
 }
 
 // Row path for rows of at most kRowCap slots (16-byte aligned): the row is
 // read once with 16-byte loads into LDS as order keys, building the first
 // digit's histogram on the way; later digits and the output pass run on LDS.
-// Outputs are compacted per round of NT slots (wave ballots, the waves'
-// counts summed through LDS), in slot order.
+// Outputs are placed in slot order by emit_row (one barrier per row).
 __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
     int32_t k, int32_t window, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
@@ -254,7 +339,7 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     __shared__ __attribute__((aligned(16))) uint32_t keys[kRowCap];
     __shared__ int hist[kBins];
     __shared__ int wave_tot[NT / 64];
-    __shared__ int wcnt[2][2][NT / 64];
+    __shared__ int wcnt[2][NT / 64];
     __shared__ int sh_digit, sh_above;
 
     const int r = (int)(gridDim.x - 1 - blockIdx.x);  // long rows first
@@ -321,34 +406,8 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
         if (exact) break;
     }
 
-    const int n_gt = k - remaining;
-    int carry_gt = 0, carry_eq = 0, parity = 0;
-    for (int s0 = 0; s0 < nv; s0 += NT) {  // uniform trip count
-        const int s = s0 + t;
-        uint32_t key = 0;
-        bool gt = false, eq = false;
-        if (s < nv) {
-            key = keys[s];
-            gt = (key & pmask) > prefix;
-            eq = (key & pmask) == prefix;
-        }
-        int rg, re, tg, te;
-        round_ranks<NT>(gt, eq, wcnt, parity, &rg, &re, &tg, &te);
-        int pos = -1;
-        if (gt) {
-            pos = carry_gt + rg;
-        } else if (eq) {
-            const int tk = carry_eq + re;
-            if (tk < remaining) pos = n_gt + tk;
-        }
-        if (pos >= 0) {
-            orow[pos] = emit(s, wstart);
-            if (osc) osc[pos] = key_to_f32(key);
-        }
-        carry_gt += tg;
-        carry_eq += te;
-        parity ^= 1;
-    }
+    emit_row<NT>([&](int s) { return *reinterpret_cast<const u32x4*>(keys + s); }, nv, prefix, pmask, k, remaining,
+                 wstart, wcnt, orow, osc);
 }
 
 // ---------------------------------------------------------------- chunked path
@@ -548,42 +607,50 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     __shared__ int pre_gt[kMaxChunks + 1];  // exclusive prefix sums of the chunks' counts
     __shared__ int pre_eq[kMaxChunks + 1];
     __shared__ int wave_tot[NT / 64];
+    __shared__ long long wave_tot64[NT / 64];
     __shared__ int wcnt[2][2][NT / 64];
     __shared__ int sh_digit, sh_above;
 
     const int r = blockIdx.x;
-    const uint32_t d1 = ghist[(size_t)r * kHeaderWords + kBins + kCoarse + 2];  // read with the position
+    const int t = threadIdx.x;
+    const int2* __restrict__ crow = counts + (size_t)r * n_counts;
+    // the threshold bin, the first NT chunk counts and the position, read together
+    const uint32_t d1 = ghist[(size_t)r * kHeaderWords + kBins + kCoarse + 2];
+    const int2 n_first = t < n_counts ? crow[t] : make_int2(0, 0);
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     if (nv <= k) return;  // uniform
     const int width = k + window;
     const int wstart = nv - window;
     int32_t* __restrict__ orow = out_idx + (size_t)r * width;
     float* __restrict__ osc = out_scores ? out_scores + (size_t)r * k : nullptr;
-    const int t = threadIdx.x;
     const int nch = (nv + CHUNK - 1) / CHUNK;  // chunks the filter filled (<= kMaxChunks)
-    const int2* __restrict__ crow = counts + (size_t)r * n_counts;
     const int2* __restrict__ rbase = cand + (size_t)r * S_max;
 
-    // prefix sums of the chunk counts, 256 chunks per round
-    int carry_gt = 0, carry_eq = 0;
+    // prefix sums of the chunk counts (both counts in one 64-bit scan), 256 chunks per round
+    long long carry = 0;  // gt total | eq total << 32
     for (int c0 = 0; c0 < nch; c0 += NT) {
         const int c = c0 + t;
-        const int2 n = c < nch ? crow[c] : make_int2(0, 0);
-        const int ig = block_inclusive_scan<NT>(n.x, wave_tot);
-        int tg = 0;
+        const int2 n = c >= nch ? make_int2(0, 0) : (c0 == 0 ? n_first : crow[c]);
+        const long long v = (long long)n.x | ((long long)n.y << 32);
+        long long x = v;
 #pragma unroll
-        for (int i = 0; i < NT / 64; ++i) tg += wave_tot[i];
-        __syncthreads();
-        const int ie = block_inclusive_scan<NT>(n.y, wave_tot);
-        int te = 0;
-#pragma unroll
-        for (int i = 0; i < NT / 64; ++i) te += wave_tot[i];
-        if (c < nch) {
-            pre_gt[c + 1] = carry_gt + ig;
-            pre_eq[c + 1] = carry_eq + ie;
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(x, off, 64);
+            if ((t & 63) >= off) x += y;
         }
-        carry_gt += tg;
-        carry_eq += te;
+        if ((t & 63) == 63) wave_tot64[t >> 6] = x;
+        __syncthreads();
+        long long add = carry, tot = carry;
+#pragma unroll
+        for (int i = 0; i < NT / 64; ++i) {
+            add += i < (t >> 6) ? wave_tot64[i] : 0;
+            tot += wave_tot64[i];
+        }
+        if (c < nch) {
+            pre_gt[c + 1] = (int)(add + x);
+            pre_eq[c + 1] = (int)((add + x) >> 32);
+        }
+        carry = tot;
         __syncthreads();
     }
     if (t == 0) {
@@ -591,8 +658,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
         pre_eq[0] = 0;
     }
     __syncthreads();
-    const int total_gt = carry_gt;  // slots above the threshold bin
-    const int n_cand = carry_eq;    // slots in it
+    const int total_gt = (int)carry;     // slots above the threshold bin
+    const int n_cand = (int)(carry >> 32);  // slots in it
     // chunk holding entry j of a prefix table: the largest c with pre[c] <= j
     auto chunk_of = [&](const int* pre, int j) -> int {
         int lo = 0, hi = nch;  // pre[lo] <= j < pre[hi]
@@ -609,16 +676,47 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
         return rbase[c * CHUNK + (pre_gt[c + 1] - pre_gt[c]) + (i - pre_eq[c])];
     };
 
-    // slots above the threshold bin: output columns [0, total_gt) in chunk order
-    for (int j = t; j < total_gt; j += NT) {
-        const int c = chunk_of(pre_gt, j);
-        const int2 e = rbase[c * CHUNK + (j - pre_gt[c])];
-        orow[j] = emit(e.y, wstart);
-        if (osc) osc[j] = key_to_f32((uint32_t)e.x);
-    }
+    // Source index (in the row's candidate regions) of every entry, written
+    // by the wave that owns the chunk: above-threshold entries into hist
+    // (free until the digit passes; total_gt < k <= kBins), bin candidates
+    // into lcand[].x when they fit in LDS.
     const bool in_lds = n_cand <= kResolveCap;
-    if (in_lds)
-        for (int i = t; i < n_cand; i += NT) lcand[i] = cand_global(i);
+    {
+        const int lane = t & 63;
+        for (int c = t >> 6; c < nch; c += NT / 64) {
+            const int g0 = pre_gt[c], ng = pre_gt[c + 1] - g0;
+            for (int i = lane; i < ng; i += 64) hist[g0 + i] = c * CHUNK + i;
+            if (in_lds) {
+                const int e0 = pre_eq[c], ne = pre_eq[c + 1] - e0;
+                for (int i = lane; i < ne; i += 64) lcand[e0 + i].x = c * CHUNK + ng + i;
+            }
+        }
+    }
+    __syncthreads();
+    // The slots above the threshold bin go to output columns [0, total_gt) in
+    // chunk order; the first candidates come into LDS.  All loads are issued
+    // before the first store.
+    constexpr int kMaxPer = DSA_MAX_TOPK / NT;
+    int2 ea[kMaxPer], ec[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+        const int j = t + u * NT;
+        ea[u] = make_int2(0, -1);
+        if (j < total_gt) ea[u] = rbase[hist[j]];
+        ec[u] = make_int2(0, 0);
+        if (in_lds && j < n_cand) ec[u] = rbase[lcand[j].x];
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+        const int j = t + u * NT;
+        if (j < total_gt) {
+            orow[j] = emit(ea[u].y, wstart);
+            if (osc) osc[j] = key_to_f32((uint32_t)ea[u].x);
+        }
+        if (in_lds && j < n_cand) lcand[j] = ec[u];
+    }
+    if (in_lds)  // candidates beyond the first kMaxPer * NT (each thread rewrites only its own entries)
+        for (int i = t + kMaxPer * NT; i < n_cand; i += NT) lcand[i] = rbase[lcand[i].x];
     __syncthreads();
     auto cand_at = [&](int i) -> int2 { return in_lds ? lcand[i] : cand_global(i); };
 
