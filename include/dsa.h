@@ -75,6 +75,7 @@ typedef enum dsa_key_dtype {
 #define DSA_MAX_TOPK_SLOTS (1 << 24) /* slots per row of dsa_topk / dsa_decode_step */
 #define DSA_MAX_ATTN_DIM 576
 #define DSA_MAX_ATTN_VDIM 512 /* value features: the output accumulator holds 32 heads x 512 per wave */
+#define DSA_MAX_ATTN_HEADS 65535 /* query heads of the attention (keeps launch grids in range) */
 
 /* Library version string, e.g. "0.1.0". */
 const char* dsa_version(void);
@@ -177,11 +178,11 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
  *   lse       [B, S, Hq] fp32 output or NULL, device
  *
  * Limits: Dqk % 32 == 0, 32 <= Dqk <= 576; Dv % 16 == 0, 16 <= Dv <= min(Dqk, 512);
- * B, S, Hq, K_top >= 1; S_kv >= 1; B * S <= 65535; one sequence's KV
- * (S_kv * Dqk * 2 bytes) below 2 GiB.  The workspace (size from
- * dsa_sparse_attn_workspace_size; 0 when there are enough query tokens to
- * fill the GPU) holds per-split partial results when few tokens are given;
- * it must be 16-byte aligned.
+ * B, S, K_top >= 1; 1 <= Hq <= DSA_MAX_ATTN_HEADS; S_kv >= 1; B * S <= 65535;
+ * one sequence's KV (S_kv * Dqk * 2 bytes) below 2 GiB.  The workspace
+ * (size from dsa_sparse_attn_workspace_size; 0 when there are enough query
+ * tokens to fill the GPU, and for shapes the call rejects) holds per-split
+ * partial results when few tokens are given; it must be 16-byte aligned.
  */
 size_t dsa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
 dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idx,

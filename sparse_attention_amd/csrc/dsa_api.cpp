@@ -61,7 +61,7 @@ dsa_status_t check_sparse_attn(const void* q, const void* kv, const int32_t* idx
                                int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, const void* out, bool paged = false)
 {
     if (!q || !kv || !idx || !out) return DSA_ERR_NULL;
-    if (B < 1 || S < 1 || Hq < 1 || S_kv < 1 || K_top < 1) return DSA_ERR_SHAPE;
+    if (B < 1 || S < 1 || Hq < 1 || S_kv < 1 || K_top < 1 || Hq > DSA_MAX_ATTN_HEADS) return DSA_ERR_SHAPE;
     if (Dqk < 32 || Dqk > DSA_MAX_ATTN_DIM || Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (Dv < 16 || Dv > Dqk || Dv > DSA_MAX_ATTN_VDIM || Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if ((long long)B * S > 65535) return DSA_ERR_SHAPE;
@@ -102,14 +102,14 @@ decode_layout layout_decode(const dsa_decode_args_t* a)
     L.scores_bytes = a->scores ? 0 : (size_t)a->B * a->S_max * sizeof(float);
     L.scores_off = off;
     off += round_up(L.scores_bytes);
-    L.topk_bytes = dsa::topk_workspace_bytes(a->B, a->S_max);
+    L.topk_bytes = dsa::plan::topk_workspace_bytes(a->B, a->S_max);
     L.topk_off = off;
     off += round_up(L.topk_bytes);
     const int32_t K_top = a->index_topk + a->window;
     L.list_bytes = a->index_list ? 0 : (size_t)a->B * K_top * sizeof(int32_t);
     L.list_off = off;
     off += round_up(L.list_bytes);
-    L.attn_bytes = dsa::sparse_attn_partial_bytes(a->B, 1, a->Hq, a->Dv, K_top);
+    L.attn_bytes = dsa::plan::attn_partial_bytes(a->B, 1, a->Hq, a->Dv, K_top);
     L.attn_off = off;
     off += round_up(L.attn_bytes);
     L.total = off;
@@ -141,7 +141,7 @@ dsa_status_t check_decode(const dsa_decode_args_t* a)
     if (a->H > 128) return DSA_ERR_UNSUPPORTED;
     if (a->index_topk < 1 || a->index_topk > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
     if (a->window < 0 || a->window > a->S_max) return DSA_ERR_SHAPE;
-    if (a->Hq < 1) return DSA_ERR_SHAPE;
+    if (a->Hq < 1 || a->Hq > DSA_MAX_ATTN_HEADS) return DSA_ERR_SHAPE;
     if (a->Dqk < 32 || a->Dqk > DSA_MAX_ATTN_DIM || a->Dqk % 32 != 0) return DSA_ERR_UNSUPPORTED;
     if (a->Dv < 16 || a->Dv > a->Dqk || a->Dv > DSA_MAX_ATTN_VDIM || a->Dv % 16 != 0) return DSA_ERR_UNSUPPORTED;
     if (decode_paging(a)) {
@@ -236,7 +236,7 @@ size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk)
 {
     (void)index_topk;
     if (M < 1 || S_max < 1) return 0;
-    return dsa::topk_workspace_bytes(M, S_max);
+    return dsa::plan::topk_workspace_bytes(M, S_max);
 }
 
 dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions, int32_t valid_len,
@@ -245,7 +245,7 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
 {
     dsa_status_t s = check_topk(scores, M, S_max, index_topk, topk_idx);
     if (s != DSA_OK) return s;
-    const size_t need = dsa::topk_workspace_bytes(M, S_max);
+    const size_t need = dsa::plan::topk_workspace_bytes(M, S_max);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     return launch_status(dsa::launch_topk(scores, M, S_max, positions, valid_len, index_topk, 0, topk_idx,
                                           topk_scores, workspace, false, stream));
@@ -254,7 +254,8 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
 size_t dsa_sparse_attn_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
 {
     if (B < 1 || S < 1 || Hq < 1 || Dv < 1 || K_top < 1) return 0;
-    return dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+    if ((long long)B * S > 65535 || Hq > DSA_MAX_ATTN_HEADS || Dv > DSA_MAX_ATTN_VDIM) return 0;  // rejected by the call
+    return dsa::plan::attn_partial_bytes(B, S, Hq, Dv, K_top);
 }
 
 dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* topk_idx, int32_t B,
@@ -264,7 +265,7 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
 {
     dsa_status_t s = check_sparse_attn(q, kv, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, out);
     if (s != DSA_OK) return s;
-    const size_t need = dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+    const size_t need = dsa::plan::attn_partial_bytes(B, S, Hq, Dv, K_top);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
     return launch_status(dsa::launch_sparse_attn(q, kv, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale,
@@ -273,8 +274,11 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
 
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args)
 {
-    if (!args || args->struct_size < offsetof(dsa_decode_args_t, index_flags) || args->B < 1 || args->S_max < 1 ||
-        args->index_topk < 1 || args->window < 0 || args->Hq < 1 || args->Dv < 1)
+    // shapes the step would reject give 0 (pointers are not needed for the size)
+    if (!args || args->struct_size < offsetof(dsa_decode_args_t, index_flags) || args->B < 1 || args->B > 65535 ||
+        args->S_max < 1 || args->S_max > DSA_MAX_TOPK_SLOTS || args->index_topk < 1 ||
+        args->index_topk > DSA_MAX_TOPK || args->window < 0 || args->window > args->S_max || args->Hq < 1 ||
+        args->Hq > DSA_MAX_ATTN_HEADS || args->Dv < 1 || args->Dv > DSA_MAX_ATTN_VDIM)
         return 0;
     return layout_decode(args).total;
 }
@@ -307,12 +311,12 @@ dsa_status_t dsa_decode_step(const dsa_decode_args_t* args, void* workspace, siz
                                            args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len,
                                            args->B, args->H, args->S_max, args->index_scale, scores,
                                            static_cast<uint32_t*>(topk_ws),
-                                           dsa::topk_header_words(args->B, args->S_max), pm, stream);
+                                           dsa::plan::topk_header_words(args->B, args->S_max), pm, stream);
     } else {
         e = dsa::launch_score_decode(args->index_q, args->index_w, args->k_cache, args->k_scale,
                                      args->k_dtype == DSA_KEY_FP8_E4M3, args->positions, args->valid_len, args->B,
                                      args->H, args->S_max, args->index_scale, scores, static_cast<uint32_t*>(topk_ws),
-                                     dsa::topk_header_words(args->B, args->S_max), pm, stream);
+                                     dsa::plan::topk_header_words(args->B, args->S_max), pm, stream);
     }
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = dsa::launch_topk(scores, args->B, args->S_max, args->positions, args->valid_len, args->index_topk,
@@ -352,7 +356,7 @@ dsa_status_t dsa_sparse_attn_paged(const void* q, const void* kv_pool, const flo
     dsa::PageMap pm;
     s = check_paging(paging, S_kv, &pm);
     if (s != DSA_OK) return s;
-    const size_t need = dsa::sparse_attn_partial_bytes(B, S, Hq, Dv, K_top);
+    const size_t need = dsa::plan::attn_partial_bytes(B, S, Hq, Dv, K_top);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
     if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
     return launch_status(dsa::launch_sparse_attn(q, kv_pool, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top,

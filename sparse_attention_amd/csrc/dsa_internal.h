@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "dsa.h"
+#include "launch_plan.h"
 
 namespace dsa {
 
@@ -48,28 +49,21 @@ hipError_t launch_score_prefill(const void* q, const float* w, const void* k_cac
 
 // Top-k per row.  With window > 0 the output row has width k + window and
 // holds the top-k with in-window entries replaced by -1, followed by the
-// window positions (the decode-step index list).
-// Workspace bytes launch_topk needs for these shapes (0 for the row path),
-// and how many leading 32-bit words of it must be zero when it starts.
-size_t topk_workspace_bytes(int32_t M, int32_t S_max);
-size_t topk_header_words(int32_t M, int32_t S_max);
-// header_zeroed: the caller already cleared the header words in stream order.
+// window positions (the decode-step index list).  The workspace holds
+// plan::topk_workspace_bytes; header_zeroed: the caller already cleared its
+// first plan::topk_header_words words in stream order.
 hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
                        int32_t valid_len, int32_t k, int32_t window, int32_t* out_idx, float* out_scores,
                        void* workspace, bool header_zeroed, hipStream_t stream);
 
-// Partial-buffer size of the sparse attention launch (0 when the list is not split).
-size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
-
-// The two attention kernels behind launch_sparse_attn: many query tokens
-// (128-head workgroups fill the chip; no split, no workspace) and few (the
-// list split over workgroups, partial results in the workspace).
-bool sparse_attn_wide_fits(int32_t B, int32_t S, int32_t Hq);
+// The two attention kernels behind launch_sparse_attn (plan::attn_wide
+// picks one): many query tokens (128-head workgroups fill the chip; no
+// split, no workspace) and few (the list split over workgroups, partial
+// results in the workspace, plan::attn_partial_bytes).
 hipError_t launch_sparse_attn_wide(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                                    int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                                    int32_t K_top, float sm_scale, void* out, float* lse, const PageMap* paging,
                                    hipStream_t stream);
-size_t sparse_attn_decode_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top);
 hipError_t launch_sparse_attn_decode(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                                      int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                                      int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,

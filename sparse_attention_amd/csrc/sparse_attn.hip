@@ -13,18 +13,12 @@
 
 namespace dsa {
 
-size_t sparse_attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
-{
-    if (sparse_attn_wide_fits(B, S, Hq)) return 0;
-    return sparse_attn_decode_partial_bytes(B, S, Hq, Dv, K_top);
-}
-
 hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                               int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                               int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
                               const PageMap* paging, hipStream_t stream)
 {
-    if (sparse_attn_wide_fits(B, S, Hq))
+    if (plan::attn_wide(B, S, Hq))
         return launch_sparse_attn_wide(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out, lse,
                                        paging, stream);
     return launch_sparse_attn_decode(q, kv, attn_sink, idx, B, S, Hq, Dqk, Dv, S_kv, K_top, sm_scale, out, lse,

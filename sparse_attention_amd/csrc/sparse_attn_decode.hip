@@ -73,10 +73,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = 256;
-constexpr int kHeadsPerGroup = 64;   // 4 waves x 16 heads
-constexpr int kBlock = 32;           // index-list entries per block
-constexpr int kTargetGroups = 256;   // workgroups wanted to fill the chip
-constexpr int kMaxSplits = 8;
+constexpr int kHeadsPerGroup = plan::kDecodeHeadsPerGroup;  // 4 waves x 16 heads
+constexpr int kBlock = plan::kDecodeBlock;                  // index-list entries per block
+constexpr int kMaxSplits = plan::kDecodeMaxSplits;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
@@ -569,17 +568,6 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     }
 }
 
-int splits_for(int32_t BS, int32_t Hq, int32_t K_top)
-{
-    const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
-    const long long groups = (long long)BS * HG;
-    const int nblk = (K_top + kBlock - 1) / kBlock;
-    int ns = (int)((kTargetGroups + groups - 1) / groups);
-    ns = std::min(ns, kMaxSplits);
-    ns = std::min(ns, std::max(1, nblk / 4));  // at least 4 blocks per split
-    return std::max(ns, 1);
-}
-
 template <int KSTEPS, int VT, int ROWU, bool EXACT, bool PAGED>
 hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink, const int32_t* idx, int32_t B,
                           int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale,
@@ -587,12 +575,12 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
 {
     const int BS = B * S;
     const int HG = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
-    const int ns = splits_for(BS, Hq, K_top);
+    const int ns = plan::attn_decode_splits(BS, Hq, K_top);
     uint16_t* part_o = nullptr;
     float2* part_ml = nullptr;
-    if (ns > 1) {
+    if (ns > 1) {  // the workspace layout of plan::attn_partial_bytes
         part_o = static_cast<uint16_t*>(workspace);
-        const size_t o_bytes = ((size_t)BS * ns * Hq * Dv * sizeof(uint16_t) + 255) & ~(size_t)255;
+        const size_t o_bytes = plan::attn_decode_partial_out_bytes(BS, 1, Hq, Dv, ns);
         part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
     }
     const long long tok_per_xcd = (BS + kXcds - 1) / kXcds;
@@ -609,15 +597,6 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
 }
 
 }  // namespace
-
-size_t sparse_attn_decode_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t K_top)
-{
-    const int ns = splits_for(B * S, Hq, K_top);
-    if (ns <= 1) return 0;
-    const size_t n = (size_t)B * S * ns * Hq;
-    const size_t o_bytes = (n * Dv * sizeof(uint16_t) + 255) & ~(size_t)255;
-    return o_bytes + n * sizeof(float2);
-}
 
 hipError_t launch_sparse_attn_decode(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                                      int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,

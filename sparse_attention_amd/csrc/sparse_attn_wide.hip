@@ -65,6 +65,7 @@ constexpr int kHalf = 32;       // a block whose upper half is masked skips it
 constexpr int kWaves = 4;       // waves per workgroup, one per SIMD
 constexpr int kWaveHeads = 32;  // heads per wave
 constexpr int kHeads = kWaves * kWaveHeads;  // heads per workgroup
+static_assert(kHeads == plan::kWideHeads, "the host-side plan counts workgroups of kHeads heads");
 constexpr int kET = kBlock / 16;             // 16-entry tiles per block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaxGrowth = 16.f;  // log2 units a block max may exceed the reference max
@@ -586,11 +587,6 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
 }
 
 }  // namespace
-
-bool sparse_attn_wide_fits(int32_t B, int32_t S, int32_t Hq)
-{
-    return (long long)B * S * ((Hq + kHeads - 1) / kHeads) >= 256;
-}
 
 hipError_t launch_sparse_attn_wide(const void* q, const void* kv, const float* attn_sink, const int32_t* idx,
                                    int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,

@@ -53,15 +53,15 @@
 namespace dsa {
 namespace {
 
-constexpr int kBins = 4096;  // first / second digit: 12 bits
-constexpr int kChunk = 4096;  // slots per workgroup in the chunked path (rows longer than this are chunked)
-constexpr int kChunkSmall = 2048;  // ... when 4096-slot chunks would give fewer than kSmallGridWgs workgroups
-constexpr int kSmallGridWgs = 512;
+// sizes shared with the host-side planning (launch_plan.h)
+constexpr int kBins = plan::kTopkBins;  // first / second digit: 12 bits
+constexpr int kChunk = plan::kTopkChunk;
+constexpr int kChunkSmall = plan::kTopkChunkSmall;
 constexpr int kChunkThreads = 256;
 constexpr int kRowThreads = 1024;
-constexpr int kCoarse = 256;  // top 8 key bits: sign + 7 exponent bits
-constexpr int kCtrl = 4;      // per-row words: [2] = threshold bin of the first digit (others unused)
-constexpr int kHeaderWords = kBins + kCoarse + kCtrl;  // per-row words zeroed before each call
+constexpr int kCoarse = plan::kTopkCoarse;  // top 8 key bits: sign + 7 exponent bits
+constexpr int kHeaderWords = plan::kTopkHeaderWords;  // per-row words zeroed before each call; control word
+                                                      // kBins + kCoarse + 2 = threshold bin of the first digit
 constexpr int kResolveCap = 8192;  // candidates resolved from LDS; more are re-read from HBM
 constexpr int kRowLdsThreads = 512;
 constexpr int kRowCap = 8192;      // row path: rows up to this many slots are held in LDS
@@ -773,28 +773,14 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     }
 }
 
-bool use_chunked(int32_t M, int32_t S_max) { return S_max > kChunk && M < 1024; }
-
-// chunked-path workspace: row headers (zeroed before each call), per-chunk
-// counts (sized for the smaller chunk), candidate regions (one slot each)
-size_t count_words(int32_t S_max) { return (size_t)(S_max + kChunkSmall - 1) / kChunkSmall; }
 
 }  // namespace
-
-size_t topk_workspace_bytes(int32_t M, int32_t S_max)
-{
-    if (!use_chunked(M, S_max)) return 0;
-    return (size_t)M * kHeaderWords * sizeof(uint32_t) + (size_t)M * count_words(S_max) * sizeof(int2) +
-           (size_t)M * S_max * sizeof(int2);
-}
-
-size_t topk_header_words(int32_t M, int32_t S_max) { return use_chunked(M, S_max) ? (size_t)M * kHeaderWords : 0; }
 
 hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,
                        int32_t valid_len, int32_t k, int32_t window, int32_t* out_idx, float* out_scores,
                        void* workspace, bool header_zeroed, hipStream_t stream)
 {
-    if (!use_chunked(M, S_max)) {
+    if (!plan::topk_chunked(M, S_max)) {
         if (S_max <= kRowCap && (S_max & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0)
             topk_row_lds_kernel<<<M, kRowLdsThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, window,
                                                                   out_idx, out_scores);
@@ -804,13 +790,13 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
         return hipGetLastError();
     }
     uint32_t* ghist = static_cast<uint32_t*>(workspace);
-    const int n_counts = (int)count_words(S_max);
+    const int n_counts = (int)plan::topk_count_words(S_max);
     int2* counts = reinterpret_cast<int2*>(ghist + (size_t)M * kHeaderWords);
     int2* cand = counts + (size_t)M * n_counts;
     const int n_words = M * kHeaderWords;
     if (!header_zeroed) topk_clear_kernel<<<(n_words + 255) / 256, 256, 0, stream>>>(ghist, n_words);
     // chunk size: 4096 slots, or 2048 when that would leave the chip short of workgroups
-    if ((long long)M * ((S_max + kChunk - 1) / kChunk) < kSmallGridWgs) {
+    if (plan::topk_chunk(M, S_max) == kChunkSmall) {
         const dim3 grid((S_max + kChunkSmall - 1) / kChunkSmall, M);
         topk_hist_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(scores, S_max, positions, valid_len, k, ghist);
         topk_filter_kernel<kChunkSmall><<<grid, kChunkThreads, 0, stream>>>(
