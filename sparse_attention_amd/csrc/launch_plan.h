@@ -55,6 +55,7 @@ constexpr int kDecodeHeadsPerGroup = 64;  // heads per workgroup of the few-toke
 constexpr int kDecodeBlock = 32;          // index-list entries per block
 constexpr int kDecodeTargetGroups = 256;  // workgroups wanted to fill the chip
 constexpr int kDecodeMaxSplits = 8;
+constexpr int kDecodeMinSplitBlocks = 4;  // blocks per split at least
 
 inline bool attn_wide(int32_t B, int32_t S, int32_t Hq)
 {
@@ -62,8 +63,8 @@ inline bool attn_wide(int32_t B, int32_t S, int32_t Hq)
 }
 
 // Parts the few-token kernel cuts each index list into: enough for about
-// kDecodeTargetGroups workgroups, at most kDecodeMaxSplits, at least 4
-// blocks each.
+// kDecodeTargetGroups workgroups, at most kDecodeMaxSplits, at least
+// kDecodeMinSplitBlocks blocks each.
 inline int attn_decode_splits(long long BS, int32_t Hq, int32_t K_top)
 {
     const long long HG = ((long long)Hq + kDecodeHeadsPerGroup - 1) / kDecodeHeadsPerGroup;
@@ -71,7 +72,7 @@ inline int attn_decode_splits(long long BS, int32_t Hq, int32_t K_top)
     const long long nblk = ((long long)K_top + kDecodeBlock - 1) / kDecodeBlock;
     long long ns = (kDecodeTargetGroups + groups - 1) / groups;
     if (ns > kDecodeMaxSplits) ns = kDecodeMaxSplits;
-    const long long by_blocks = nblk / 4 > 1 ? nblk / 4 : 1;
+    const long long by_blocks = nblk / kDecodeMinSplitBlocks > 1 ? nblk / kDecodeMinSplitBlocks : 1;
     if (ns > by_blocks) ns = by_blocks;
     return ns < 1 ? 1 : (int)ns;
 }
