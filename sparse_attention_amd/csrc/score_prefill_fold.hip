@@ -48,6 +48,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 32;  // keys per tile
 constexpr int kSteps = 8;  // K steps of 16 dims
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw (byte-addressed) access
+constexpr int kStoreNt = 2;               // buffer store cache policy: non-temporal
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
 {
@@ -207,6 +209,23 @@ __global__ __launch_bounds__(kThreads) void score_prefill_fold_kernel(
     const int max_nv = max(max_nv_m[0], max_nv_m[1]);
     const float mb = mask_bound();
 
+    // Score rows of the two row tiles as buffers.  A store for a row past the
+    // tile's rows or a key past S_max gets an offset beyond the buffer bound,
+    // which the hardware drops: every store is issued unconditionally, so the
+    // compiler can count them and wait for the next key tile's loads alone
+    // (loads and stores share one in-order counter here) instead of draining
+    // the previous tile's score stores on every tile.
+    __amdgpu_buffer_rsrc_t srs[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        srs[m] = __builtin_amdgcn_make_buffer_rsrc((void*)(scores + (size_t)base_m[m] * S_max), 0,
+                                                   cnt_m[m] * S_max * 4, kBufferWord3);
+    auto store = [&](int m, int j, int s, float v) {
+        const int rl = 8 * (j / 4) + 4 * g + j % 4;  // row of tile m
+        const uint32_t off = (rl < cnt_m[m] && s < S_max) ? (uint32_t)(rl * S_max + s) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs[m], off, 0, kStoreNt);
+    };
+
     const int ntiles = (S_max + kKeys - 1) / kKeys;
     auto load_tile = [&](int kt, u32x4 (&b)[kSteps]) {
         const int s = kt * kKeys + n;
@@ -214,46 +233,48 @@ __global__ __launch_bounds__(kThreads) void score_prefill_fold_kernel(
 #pragma unroll
         for (int t = 0; t < kSteps; ++t) b[t] = *reinterpret_cast<const u32x4*>(kp + 16 * t);
     };
-    u32x4 bcur[kSteps];
+    // key tiles holding a live slot of some row of the workgroup: wave w takes
+    // tiles w, w + kWaves, ...; each iteration loads the wave's next tile (the
+    // last one again at the end, so every iteration issues the same loads)
+    const int n_live = min(ntiles, (max_nv + kKeys - 1) / kKeys);
     int kt = wave;
-    if (kt < ntiles && kt * kKeys < max_nv) load_tile(kt, bcur);
-    for (; kt < ntiles; kt += kWaves) {
-        const int s = kt * kKeys + n;
-        if (kt * kKeys >= max_nv) {
-            // every row of the workgroup is past its causal limit here: mask bound only
-            if (s < S_max)
+    if (kt < n_live) {
+        u32x4 bcur[kSteps];
+        load_tile(kt, bcur);
+        // stores past every buffer bound (dropped): each iteration then starts
+        // with the same pending operations, the next tile's loads followed by a
+        // tile's 16 stores, so the wait for the loads leaves the stores in flight
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int i = 16 * m + 8 * (j / 4) + 4 * g + j % 4;
-                        if (row_ok(i)) __builtin_nontemporal_store(mb, &scores[(size_t)grow(i) * S_max + s]);
-                    }
-            continue;
-        }
-        u32x4 b[kSteps];
+            for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, srs[m], 0x80000000u, 0, kStoreNt);
+        for (; kt < n_live; kt += kWaves) {
+            const int s = kt * kKeys + n;
+            u32x4 b[kSteps];
 #pragma unroll
-        for (int t = 0; t < kSteps; ++t) b[t] = bcur[t];
-        const int nk = kt + kWaves;
-        if (nk < ntiles && nk * kKeys < max_nv) load_tile(nk, bcur);  // next tile, one ahead
-        f32x16 c[2];
+            for (int t = 0; t < kSteps; ++t) b[t] = bcur[t];
+            load_tile(min(kt + kWaves, n_live - 1), bcur);  // the next tile, one ahead
+            f32x16 c[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            c[m] = f32x16{};
-            if (kt * kKeys < max_nv_m[m])  // uniform: skip a row tile that is all masked here
+            for (int m = 0; m < 2; ++m) {
+                c[m] = f32x16{};
+                if (kt * kKeys < max_nv_m[m])  // uniform: skip a row tile that is all masked here
 #pragma unroll
-                for (int t = 0; t < kSteps; ++t) c[m] = mfma32(qa[m][t], b[t], c[m]);
-        }
-        if (s < S_max)
+                    for (int t = 0; t < kSteps; ++t) c[m] = mfma32(qa[m][t], b[t], c[m]);
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int i = 16 * m + 8 * (j / 4) + 4 * g + j % 4;
-                    if (row_ok(i))
-                        __builtin_nontemporal_store(s < nv_r[m][j] ? c[m][j] + c[m][j + 8] : mb,
-                                                    &scores[(size_t)grow(i) * S_max + s]);
-                }
+                for (int j = 0; j < 8; ++j) store(m, j, s, s < nv_r[m][j] ? c[m][j] + c[m][j + 8] : mb);
+        }
+    }
+    // tiles past every row's causal limit: the mask bound only
+    for (kt = n_live + ((wave - n_live) % kWaves + kWaves) % kWaves; kt < ntiles; kt += kWaves) {
+        const int s = kt * kKeys + n;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) store(m, j, s, mb);
     }
 }
 
