@@ -178,19 +178,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     const int32_t* __restrict__ ilist = idx + (size_t)tok * K_top;
     const uint16_t* __restrict__ kvb = PAGED ? kv : kv + (size_t)b * S_kv * Dqk;
 
-    // q of this lane's head: B operand of QK^T (dims 32t + 8g .. +7)
-    u32x4 qreg[KSTEPS];
-    {
-        const uint16_t* qh = q + ((size_t)tok * Hq + (head_ok ? head : 0)) * Dqk + 8 * g;
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
-            qreg[t] = (head_ok && t < ksteps) ? *reinterpret_cast<const u32x4*>(qh + 32 * t) : u32x4{0, 0, 0, 0};
-        // q only ever feeds MFMAs, which read AGPRs: keeping it there leaves the
-        // VGPRs to the accumulator and to operand reads in flight
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) __asm__("" : "+a"(qreg[t]));
-    }
-
     // Every wave keeps the 32 index-list entries of a block in its lanes
     // (lane % 32 = entry).  fetch_idx issues an unconditional in-bounds load;
     // check_idx turns the loaded value into a row or -1 once it is used.
@@ -203,6 +190,27 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         const int j = (blk0 + blk) * kBlock + el;
         return (blk < nblk && j < K_top && t >= 0 && t < S_kv) ? t : -1;
     };
+    // The first two blocks' list entries go out before q: block 0's copy then
+    // waits only for its entries, and q streams in meanwhile.  (The branch,
+    // always taken, puts the loads in a block of their own; within one block
+    // the compiler would order them after the q loads.)
+    int raw0 = -1, pending = -1;
+    if (K_top > 0) {
+        raw0 = fetch_idx(0);
+        pending = fetch_idx(nblk > 1 ? 1 : 0);
+    }
+
+    // q of this lane's head: B operand of QK^T (dims 32t + 8g .. +7); moved to
+    // AGPRs once block 0's copy is issued.  Lanes of heads past Hq load head 0
+    // (their scores are never stored; heads do not mix in the MFMAs), so the
+    // exact shapes load without a branch.
+    u32x4 qreg[KSTEPS];
+    {
+        const uint16_t* qh = q + ((size_t)tok * Hq + (head_ok ? head : 0)) * Dqk + 8 * g;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+            qreg[t] = (EXACT || t < ksteps) ? *reinterpret_cast<const u32x4*>(qh + 32 * t) : u32x4{0, 0, 0, 0};
+    }
     // Issue the LDS DMA of a block's rows (entry e's row in lane e of rows_idx)
     // into dst: the block's 32 x rowu units are walked flat, 64 consecutive
     // units per wave instruction.  Iterations that are in range for every
@@ -277,8 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 
     // prologue: indices of block 0 (checked) and block 1 (in flight), rows of block 0
     // (paged: block 1 checked with its table lookup in flight, block 2 in flight)
-    int cur_idx = check_idx(0, fetch_idx(0));
-    int pending = fetch_idx(nblk > 1 ? 1 : 0);
+    int cur_idx = check_idx(0, raw0);
     int nxt_page = 0;
     if (PAGED) {
         const int page0 = fetch_page(cur_idx);
@@ -287,10 +294,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
         pending = check_idx(1, pending);  // block 1: checked slot ...
         nxt_page = fetch_page(pending);   // ... and its table entry, in flight
         // the raw entries of block 2 travel in nxt_raw
-    } else if (nblk > 0) {
-        gather(cur_idx, kvbuf0);
+    } else {
+        gather(cur_idx, kvbuf0);  // unconditional (an empty split copies row 0), so raw0's load stays first
     }
     int nxt_raw = PAGED ? fetch_idx(nblk > 2 ? 2 : 0) : 0;
+    // q only ever feeds MFMAs, which read AGPRs: keeping it there leaves the
+    // VGPRs to the accumulator and to operand reads in flight.  (This waits for
+    // the q loads, which were issued before block 0's copy.)
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) __asm__("" : "+a"(qreg[t]));
 
     // One block: its rows are in kb (a compile-time choice of kvbuf0 / kvbuf1,
     // so the compiler can tell the DMA into the other buffer never aliases
