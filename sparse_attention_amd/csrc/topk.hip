@@ -433,10 +433,24 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     constexpr int kPer = CHUNK / kChunkThreads;  // slots per thread: loads first, then LDS atomics
     const int sl = min(s0 + CHUNK, S_max);
     float v[kPer];
+    // 16-byte loads when the row is 16-byte aligned (slots s0 + 4 (i * NT + t) + e), else 4-byte ones
+    const bool wide = ((reinterpret_cast<uintptr_t>(row) | (uintptr_t)S_max * 4) & 15) == 0;
+    auto slot_of = [&](int i) {
+        return wide ? s0 + 4 * ((i >> 2) * kChunkThreads + (int)threadIdx.x) + (i & 3) : s0 + i * kChunkThreads + (int)threadIdx.x;
+    };
+    if (wide) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int s = s0 + i * kChunkThreads + (int)threadIdx.x;
-        v[i] = s < sl ? row[s] : 0.f;
+        for (int i = 0; i < kPer; i += 4) {
+            const int s = slot_of(i);
+            const float4 x = s < sl ? *reinterpret_cast<const float4*>(row + s) : float4{0.f, 0.f, 0.f, 0.f};
+            v[i] = x.x; v[i + 1] = x.y; v[i + 2] = x.z; v[i + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int s = slot_of(i);
+            v[i] = s < sl ? row[s] : 0.f;
+        }
     }
     const int nv = n_valid_of(positions, valid_len, r, S_max);
     if (nv <= k || s0 >= nv) return;  // uniform
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-        if (s0 + i * kChunkThreads + (int)threadIdx.x < s1) atomicAdd(&hist[f32_order_key(v[i]) >> 20], 1);
+        if (slot_of(i) < s1) atomicAdd(&hist[f32_order_key(v[i]) >> 20], 1);
     __syncthreads();
     uint32_t* __restrict__ gh = ghist + (size_t)r * kHeaderWords;
     for (int i = threadIdx.x; i < kBins; i += kChunkThreads) {
