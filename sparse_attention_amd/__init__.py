@@ -276,12 +276,19 @@ class DecodeStep:
     """Reusable dsa_decode_step call: validates shapes once, owns the workspace and outputs.
 
     With ``static_scratch`` the step calls dsa_decode_step_static instead: no workspace is allocated and the
-    library's per-GPU scratch array (DSA_STATIC_SCRATCH_BYTES) is used; calls on one GPU must not overlap."""
+    library's per-GPU scratch array (DSA_STATIC_SCRATCH_BYTES) is used; calls on one GPU must not overlap.
+
+    With ``graph`` the first call runs the step once and captures it into a HIP graph (the library issues only
+    kernel launches on the caller's stream: no allocation, memset or synchronisation), and every later call
+    replays that graph: one host call per step instead of one kernel launch per stage.  The graph reads and
+    writes the buffers given here, so new inputs are written into them in place (as a serving loop does with
+    its caches and query buffers)."""
 
     def __init__(self, index_q, index_w, k_cache, *, positions=None, valid_len: int = -1, index_scale: float,
                  index_topk: int, window: int, q, kv, attn_sink, sm_scale: float, dv: int, k_scale=None,
                  keep_scores: bool = True, keep_index_list: bool = True, relu: bool = False,
-                 paging: Optional[Paging] = None, s_max: Optional[int] = None, static_scratch: bool = False):
+                 paging: Optional[Paging] = None, s_max: Optional[int] = None, static_scratch: bool = False,
+                 graph: bool = False):
         _dev(index_q, "index_q", (torch.bfloat16,))
         _dev(index_w, "index_w", (torch.float32,))
         _dev(k_cache, "k_cache", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn))
@@ -327,14 +334,29 @@ class DecodeStep:
         self.static_scratch = bool(static_scratch)
         self._nws = lib.dsa_decode_step_workspace_size(ctypes.byref(a))
         self._ws = None if self.static_scratch else _workspace(self._nws, dev)
+        self.use_graph = bool(graph)
+        self._graph = None
 
-    def __call__(self):
+    def _launch(self):
         lib = load_library()
         if self.static_scratch:
             _check("dsa_decode_step_static", lib.dsa_decode_step_static(ctypes.byref(self._args), _stream()))
+        else:
+            _check("dsa_decode_step", lib.dsa_decode_step(ctypes.byref(self._args), _ptr(self._ws), self._nws,
+                                                          _stream()))
+
+    def __call__(self):
+        if not self.use_graph:
+            self._launch()
             return self.out
-        st = lib.dsa_decode_step(ctypes.byref(self._args), _ptr(self._ws), self._nws, _stream())
-        _check("dsa_decode_step", st)
+        if self._graph is None:
+            self._launch()  # validates the arguments and loads the kernels outside the capture
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._launch()
+            self._graph = g
+        self._graph.replay()
         return self.out
 
 

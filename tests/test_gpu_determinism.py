@@ -136,3 +136,35 @@ def test_decode_step_repeat(dsa, relu):
         for a, b, what in zip(first, (step.scores, step.index_list, step.out, step.lse),
                               ("scores", "index list", "output", "lse")):
             _same(a, b, "decode step " + what)
+
+
+@pytest.mark.parametrize("static_scratch", [False, True])
+def test_decode_step_graph_replays(dsa, static_scratch):
+    """A step captured in a HIP graph: every replay equals an eager step on the same inputs, with eager work and
+    synchronisations between replays, and replays follow inputs rewritten in place (new positions)."""
+    w = synthetic.make_workload("full_decode_step", B=16, S_max=32768, topk=1024, window=128)
+    announce("graph replay: dsa_decode_step B=%d S_max=%d static_scratch=%s" % (w.M, w.S_max, static_scratch))
+    ins = dict(index_q=_cuda(w.index_q), index_w=_cuda(w.index_w), k_cache=_cuda(w.k_cache),
+               positions=_cuda(w.positions), q=_cuda(w.q), kv=_cuda(w.kv), attn_sink=_cuda(w.sink))
+    kw = dict(valid_len=w.valid_len, index_scale=w.index_scale, index_topk=w.index_topk, window=w.window,
+              sm_scale=w.sm_scale, dv=w.dv)
+    eager = dsa.DecodeStep(ins["index_q"], ins["index_w"], ins["k_cache"], positions=ins["positions"],
+                           q=ins["q"], kv=ins["kv"], attn_sink=ins["attn_sink"], **kw)
+    graphed = dsa.DecodeStep(ins["index_q"], ins["index_w"], ins["k_cache"], positions=ins["positions"],
+                             q=ins["q"], kv=ins["kv"], attn_sink=ins["attn_sink"], static_scratch=static_scratch,
+                             graph=True, **kw)
+    outs = lambda st: (st.scores, st.index_list, st.out, st.lse)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for rep in range(4):
+        if rep == 2:  # new positions, written in place into the buffer both steps read
+            ins["positions"].copy_(torch.randint(1000, w.S_max, (w.M,), generator=g, dtype=torch.int32))
+        eager()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs(eager)]
+        _disturb()
+        graphed()
+        torch.cuda.synchronize()
+        for a, b, what in zip(ref, outs(graphed), ("scores", "index list", "output", "lse")):
+            _same(a, b, "graph replay %d %s" % (rep, what))
+        _disturb()
+        torch.cuda.synchronize()
