@@ -33,7 +33,9 @@
 //   * q (read once) and the score matrix (written once) stream with
 //     non-temporal loads and stores, so they do not displace the keys in
 //     L2: with plain ones the q fold read at ~3.1 TB/s and the kernel took
-//     144 us at 8192 x 8192, against 22 us for the fold and 108 us.
+//     144 us at 8192 x 8192, against 22 us for the fold and 108 us.  The
+//     score stores also carry device scope (sc1): 97 against 99.5 us, the
+//     scores bit-equal; plain or sc0 stores took 121-125 us.
 #include "device_common.h"
 #include "dsa_internal.h"
 
@@ -49,7 +51,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 32;  // keys per tile
 constexpr int kSteps = 8;  // K steps of 16 dims
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data, raw (byte-addressed) access
-constexpr int kStoreNt = 2;               // buffer store cache policy: non-temporal
+constexpr int kStoreNt = 18;              // buffer store cache policy: non-temporal, device scope (nt sc1)
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
 {
