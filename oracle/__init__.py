@@ -11,6 +11,8 @@ Functions follow the web pages cited in ``dsa_oracle.c``:
   * ``topk``         -- full-sort top-k (unordered-set contract), -1 padding
   * ``assemble``     -- top-k plus always-selected sliding window
   * ``sparse_attn``  -- two-pass softmax-with-sink attention over an index list
+  * ``masked_dense_attn`` -- the same attention over the set of listed slots,
+                        as a dense masked pass over every slot
   * ``n_valid``      -- attendable slots of a row
   * ``quantize_fp8_blocks`` / ``dequantize_fp8_blocks`` -- FP8 E4M3 block
                         quantiser (binary32 decisions, nearest code, ties even)
@@ -61,6 +63,8 @@ def _load():
     lib.oracle_topk.argtypes = [vp, i32, i32, vp, i32, i32, vp, vp, ip]
     lib.oracle_assemble.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
     lib.oracle_sparse_attn.argtypes = [vp, ip, vp, ip, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, vp, vp, ip]
+    lib.oracle_masked_dense_attn.argtypes = [vp, ip, vp, ip, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, vp, vp,
+                                             ip]
     lib.oracle_encode_fp8_e4m3.argtypes = [vp, vp, i64]
     lib.oracle_quantize_fp8_blocks.argtypes = [vp, i64, i32, ip, vp, vp]
     lib.oracle_dequantize_fp8_blocks.argtypes = [vp, vp, i64, i32, vp]
@@ -213,6 +217,28 @@ def sparse_attn(q, kv, sink, idx, *, sm_scale: float, dv: int, nthreads: int | N
     lse = np.empty((B, S, Hq), np.float64)
     _load().oracle_sparse_attn(_ptr(qa), qt, _ptr(ka), kt, _ptr(sk), _ptr(ia), B, S, Hq, Dqk, dv, S_kv, K_top,
                                float(sm_scale), _ptr(out), _ptr(lse), nthreads or default_threads())
+    return out, lse
+
+
+def masked_dense_attn(q, kv, sink, idx, *, sm_scale: float, dv: int, nthreads: int | None = None):
+    """Masked dense attention with sink (OpenXLA tokamax "Supported Ops and Hardware", masked_dense_mla):
+    every slot of the sequence, masked unless the list selects it (a slot listed twice counts once).
+    Shapes and results as ``sparse_attn``."""
+    qa, qt = _raw(q)
+    ka, kt = _raw(kv)
+    B, S, Hq, Dqk = qa.shape
+    Bk, S_kv, Dk = ka.shape
+    assert Bk == B and Dk == Dqk and 0 < dv <= Dqk
+    ia = _np(idx, np.int32)
+    assert ia.shape[:2] == (B, S)
+    K_top = ia.shape[2]
+    sk = _np(sink, np.float32)
+    if sk is not None:
+        assert sk.shape == (Hq,)
+    out = np.empty((B, S, Hq, dv), np.float64)
+    lse = np.empty((B, S, Hq), np.float64)
+    _load().oracle_masked_dense_attn(_ptr(qa), qt, _ptr(ka), kt, _ptr(sk), _ptr(ia), B, S, Hq, Dqk, dv, S_kv, K_top,
+                                     float(sm_scale), _ptr(out), _ptr(lse), nthreads or default_threads())
     return out, lse
 
 

@@ -22,6 +22,8 @@
  *   [V4-KERNEL]  kwkr.cn article on the DeepSeek-V4-Pro-0813-nvfp4-DSpark
  *                inference/kernel.py -- sections on the FP8 block quantiser
  *                and on the TileLang sparse-attention kernel.
+ *   [TOKAMAX]    OpenXLA tokamax "Supported Ops and Hardware", Attention
+ *                Variants table -- masked_dense_mla row.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - per-head activation: identity by default (the pages only say the
@@ -404,5 +406,76 @@ void oracle_sparse_attn(const void* q, int q_dtype, const void* kv, int kv_dtype
         if (lse)
             lse[item] = m + log(l);
         free(logit);
+    }
+}
+
+/*
+ * Masked dense attention [TOKAMAX] masked_dense_mla: the attention of
+ * oracle_sparse_attn over the SET of slots the list selects, written as a
+ * dense pass over every slot t < S_kv of the sequence with a boolean mask.
+ * mask[t] is set when some entry of the list equals t (entries that are -1
+ * or outside [0, S_kv) set nothing; a slot listed twice is set once).  Then,
+ * over the selected slots in slot order,
+ *   m = max_t logit_t,  l = sum_t e^{logit_t - m} + e^{sink - m},
+ *   out = sum_t e^{logit_t - m} kv[b, t, 0:Dv] / l,  lse = m + log l,
+ * the same formula as the sparse form; no selected slot: out = 0, lse = sink.
+ */
+void oracle_masked_dense_attn(const void* q, int q_dtype, const void* kv, int kv_dtype, const float* sink,
+                              const int32_t* idx, int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv,
+                              int32_t S_kv, int32_t K_top, double sm_scale, double* out, double* lse, int nthreads)
+{
+    const int64_t n_items = (int64_t)B * S * Hq;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t item = 0; item < n_items; ++item) {
+        const int32_t h = (int32_t)(item % Hq);
+        const int64_t bs = item / Hq; /* b * S + s */
+        const int64_t b = bs / S;
+        const int32_t* ilist = idx + bs * K_top;
+        unsigned char* mask = (unsigned char*)calloc((size_t)S_kv, 1);
+        double* logit = (double*)malloc(sizeof(double) * (size_t)S_kv);
+        for (int32_t j = 0; j < K_top; ++j) {
+            const int32_t t = ilist[j];
+            if (t >= 0 && t < S_kv)
+                mask[t] = 1;
+        }
+        double m = -INFINITY;
+        int32_t n_sel = 0;
+        for (int32_t t = 0; t < S_kv; ++t) {
+            if (!mask[t])
+                continue;
+            double dot = 0.0;
+            for (int32_t d = 0; d < Dqk; ++d)
+                dot += load_elem(q, q_dtype, item * Dqk + d) *
+                       load_elem(kv, kv_dtype, (b * S_kv + t) * (int64_t)Dqk + d);
+            logit[t] = sm_scale * dot;
+            if (logit[t] > m)
+                m = logit[t];
+            ++n_sel;
+        }
+        double* o = out + item * Dv;
+        for (int32_t d = 0; d < Dv; ++d)
+            o[d] = 0.0;
+        if (n_sel == 0) {
+            if (lse)
+                lse[item] = sink ? (double)sink[h] : -INFINITY;
+        } else {
+            double l = 0.0;
+            for (int32_t t = 0; t < S_kv; ++t) {
+                if (!mask[t])
+                    continue;
+                const double p = exp(logit[t] - m);
+                l += p;
+                for (int32_t d = 0; d < Dv; ++d)
+                    o[d] += p * load_elem(kv, kv_dtype, (b * S_kv + t) * (int64_t)Dqk + d);
+            }
+            if (sink)
+                l += exp((double)sink[h] - m);
+            for (int32_t d = 0; d < Dv; ++d)
+                o[d] /= l;
+            if (lse)
+                lse[item] = m + log(l);
+        }
+        free(logit);
+        free(mask);
     }
 }
