@@ -9,6 +9,9 @@
  *                     with the always-selected sliding window
  *   dsa_cache_write   new keys stored in the key cache at their positions,
  *                     optionally FP8 block-quantised
+ *   dsa_sparse_attn_masked_dense
+ *                     the same attention over the set of listed slots,
+ *                     computed densely over a short sequence
  *   dsa_index_score_paged, dsa_sparse_attn_paged, dsa_cache_write_paged
  *                     the decode scorer, the attention and the key write
  *                     over paged caches (a block table into a page pool)
@@ -21,7 +24,8 @@
  *   [V4-KERNEL] kwkr.cn article on DeepSeek-V4-Pro-0813-nvfp4-DSpark
  *               inference/kernel.py (sparse-attention and FP8 sections)
  *   [TOKAMAX]   OpenXLA tokamax "Supported Ops and Hardware", Attention
- *               Variants table (lightning_indexer, batched_rpa rows)
+ *               Variants table (lightning_indexer, batched_rpa,
+ *               masked_dense_mla rows)
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE memory on the current HIP device, owned by
@@ -76,6 +80,7 @@ typedef enum dsa_key_dtype {
 #define DSA_MAX_ATTN_DIM 576
 #define DSA_MAX_ATTN_VDIM 512 /* value features: the output accumulator holds 32 heads x 512 per wave */
 #define DSA_MAX_ATTN_HEADS 65535 /* query heads of the attention (keeps launch grids in range) */
+#define DSA_MASKED_DENSE_MAX_SLOTS 65536 /* sequence length of dsa_sparse_attn_masked_dense */
 
 /* Library version string, e.g. "0.1.0". */
 const char* dsa_version(void);
@@ -189,6 +194,34 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
                              int32_t B, int32_t S, int32_t Hq, int32_t Dqk, int32_t Dv, int32_t S_kv,
                              int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_attn_masked_dense -- the attention of dsa_sparse_attn over the
+ * SET of slots topk_idx lists, computed densely: every slot p < S_kv of the
+ * sequence enters the softmax in slot order and is masked unless listed
+ * ([TOKAMAX] masked_dense_mla row: latent attention restricted to a selected
+ * top-k subset through a dense mask, for shorter sequences).  Entries that
+ * are -1 or outside [0, S_kv) select nothing; a slot listed more than once
+ * counts once (dsa_sparse_attn counts every entry, so the two agree on
+ * lists without repeats, such as dsa_topk's).  q, kv, attn_sink, out, lse
+ * and the formulas are those of dsa_sparse_attn, with j running over the
+ * selected slots.
+ *
+ * The work grows with S_kv (all slots are read and scored), not with K_top:
+ * the form pays when the selection covers much of a short sequence.
+ *
+ * Limits: as dsa_sparse_attn, and S_kv <= DSA_MASKED_DENSE_MAX_SLOTS.  The
+ * workspace (always needed; size from
+ * dsa_sparse_attn_masked_dense_workspace_size, 0 for shapes the call
+ * rejects) holds the dense mask of every query token as a slot list
+ * (B * S * S_kv int32) and the attention's partial results; it must be
+ * 16-byte aligned.
+ */
+size_t dsa_sparse_attn_masked_dense_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t S_kv);
+dsa_status_t dsa_sparse_attn_masked_dense(const void* q, const void* kv, const float* attn_sink,
+                                          const int32_t* topk_idx, int32_t B, int32_t S, int32_t Hq, int32_t Dqk,
+                                          int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale, void* out,
+                                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Paged caches ([TOKAMAX] lightning_indexer scores over a paged KV cache;

@@ -94,6 +94,11 @@ def load_library(path: Optional[str] = None):
     lib.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.dsa_sparse_attn.restype = st
     lib.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.dsa_sparse_attn_masked_dense_workspace_size.restype = sz
+    lib.dsa_sparse_attn_masked_dense_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.dsa_sparse_attn_masked_dense.restype = st
+    lib.dsa_sparse_attn_masked_dense.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                                 sz, vp]
     lib.dsa_decode_step_workspace_size.restype = sz
     lib.dsa_decode_step_workspace_size.argtypes = [ctypes.POINTER(_DecodeArgs)]
     lib.dsa_decode_step.restype = st
@@ -267,6 +272,42 @@ def dsa_sparse_attn(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, wit
                                  K_top, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), nws, _stream())
         _check("dsa_sparse_attn", st)
     return (out, lse) if with_lse else out
+
+
+def dsa_sparse_attn_masked_dense(q, kv, attn_sink, topk_idx, *, sm_scale: float, dv: int, with_lse: bool = False,
+                                 out=None, workspace=None):
+    """The attention of dsa_sparse_attn over the set of listed slots, computed densely over all S_kv slots
+    (a slot listed twice counts once).  Arguments and results as dsa_sparse_attn; ``workspace`` (uint8, at
+    least masked_dense_workspace_bytes) may be given to avoid an allocation."""
+    _dev(q, "q", (torch.bfloat16,))
+    _dev(kv, "kv", (torch.bfloat16,))
+    _dev(topk_idx, "topk_idx", (torch.int32,))
+    if attn_sink is not None:
+        _dev(attn_sink, "attn_sink", (torch.float32,))
+    B, S, Hq, Dqk = q.shape
+    S_kv = kv.shape[1]
+    K_top = topk_idx.shape[2]
+    lib = load_library()
+    if out is None:
+        out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", (torch.bfloat16,))
+    if tuple(out.shape) != (B, S, Hq, dv):
+        raise ValueError("out must be [B, S, Hq, dv]")
+    lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device) if with_lse else None
+    nws = lib.dsa_sparse_attn_masked_dense_workspace_size(B, S, Hq, int(dv), S_kv)
+    ws = workspace if workspace is not None else _workspace(nws, q.device)
+    if nws and (ws is None or ws.numel() * ws.element_size() < nws):
+        raise ValueError("workspace must hold %d bytes" % nws)
+    st = lib.dsa_sparse_attn_masked_dense(_ptr(q), _ptr(kv), _ptr(attn_sink), _ptr(topk_idx), B, S, Hq, Dqk,
+                                          int(dv), S_kv, K_top, float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), nws,
+                                          _stream())
+    _check("dsa_sparse_attn_masked_dense", st)
+    return (out, lse) if with_lse else out
+
+
+def masked_dense_workspace_bytes(B: int, S: int, Hq: int, dv: int, S_kv: int) -> int:
+    return int(load_library().dsa_sparse_attn_masked_dense_workspace_size(int(B), int(S), int(Hq), int(dv),
+                                                                          int(S_kv)))
 
 
 DSA_STATIC_SCRATCH_BYTES = 128 << 20

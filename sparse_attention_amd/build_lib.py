@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 
 HIP_SOURCES = ["score_decode.hip", "score_decode_heads.hip", "score_prefill.hip", "topk.hip", "sparse_attn.hip",
-               "sparse_attn_decode.hip", "sparse_attn_wide.hip", "cache_write.hip", "score_prefill_fold.hip", "decode_static.hip"]
+               "sparse_attn_decode.hip", "sparse_attn_wide.hip", "cache_write.hip", "score_prefill_fold.hip", "decode_static.hip",
+               "attn_masked_dense.hip"]
 CPP_SOURCES = ["dsa_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]

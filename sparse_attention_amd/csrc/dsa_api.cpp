@@ -272,6 +272,29 @@ dsa_status_t dsa_sparse_attn(const void* q, const void* kv, const float* attn_si
                                                  out, lse, workspace, nullptr, stream));
 }
 
+size_t dsa_sparse_attn_masked_dense_workspace_size(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t S_kv)
+{
+    if (B < 1 || S < 1 || Hq < 1 || Hq > DSA_MAX_ATTN_HEADS || Dv < 1 || Dv > DSA_MAX_ATTN_VDIM || S_kv < 1 ||
+        S_kv > DSA_MASKED_DENSE_MAX_SLOTS || (long long)B * S > 65535)
+        return 0;
+    return dsa::plan::masked_dense_workspace_bytes(B, S, Hq, Dv, S_kv);
+}
+
+dsa_status_t dsa_sparse_attn_masked_dense(const void* q, const void* kv, const float* attn_sink,
+                                          const int32_t* topk_idx, int32_t B, int32_t S, int32_t Hq, int32_t Dqk,
+                                          int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale, void* out,
+                                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    dsa_status_t s = check_sparse_attn(q, kv, topk_idx, B, S, Hq, Dqk, Dv, S_kv, K_top, out);
+    if (s != DSA_OK) return s;
+    if (S_kv > DSA_MASKED_DENSE_MAX_SLOTS) return DSA_ERR_SHAPE;
+    const size_t need = dsa::plan::masked_dense_workspace_bytes(B, S, Hq, Dv, S_kv);
+    if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+    return launch_status(dsa::launch_sparse_attn_masked_dense(q, kv, attn_sink, topk_idx, B, S, Hq, Dqk, Dv, S_kv,
+                                                              K_top, sm_scale, out, lse, workspace, stream));
+}
+
 size_t dsa_decode_step_workspace_size(const dsa_decode_args_t* args)
 {
     // shapes the step would reject give 0 (pointers are not needed for the size)

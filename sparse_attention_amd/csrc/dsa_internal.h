@@ -74,6 +74,15 @@ hipError_t launch_sparse_attn(const void* q, const void* kv, const float* attn_s
                               int32_t K_top, float sm_scale, void* out, float* lse, void* workspace,
                               const PageMap* paging, hipStream_t stream);
 
+// Masked-dense form of launch_sparse_attn: the listed slots of each token
+// become a dense list of all S_kv slots (-1 where not selected) in the
+// workspace (plan::masked_dense_list_bytes), then the sparse attention runs
+// over it (its partials follow the list in the workspace).
+hipError_t launch_sparse_attn_masked_dense(const void* q, const void* kv, const float* attn_sink,
+                                           const int32_t* topk_idx, int32_t B, int32_t S, int32_t Hq, int32_t Dqk,
+                                           int32_t Dv, int32_t S_kv, int32_t K_top, float sm_scale, void* out,
+                                           float* lse, void* workspace, hipStream_t stream);
+
 // Key-cache write of T tokens (128 bf16 elements each): fp8 codes + scale,
 // bf16 copy, or bf16 quantised and dequantised (qdq).
 hipError_t launch_cache_write(const void* k_new, int32_t T, int32_t rows_per_seq, const int32_t* positions,

@@ -92,5 +92,16 @@ inline size_t attn_partial_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, i
     return attn_decode_partial_out_bytes(B, S, Hq, Dv, ns) + (size_t)B * S * ns * Hq * 8;
 }
 
+// ---- masked-dense attention (attn_masked_dense.hip): the dense slot list
+// of every query token, then the attention's partials for a list of S_kv entries
+inline size_t masked_dense_list_bytes(int32_t B, int32_t S, int32_t S_kv)
+{
+    return ((size_t)B * S * S_kv * 4 + 255) / 256 * 256;
+}
+inline size_t masked_dense_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Dv, int32_t S_kv)
+{
+    return masked_dense_list_bytes(B, S, S_kv) + attn_partial_bytes(B, S, Hq, Dv, S_kv);
+}
+
 }  // namespace plan
 }  // namespace dsa

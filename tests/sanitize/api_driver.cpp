@@ -92,6 +92,25 @@ int main()
     EXPECT(dsa_sparse_attn(P(A), P(A), f, io, 70000, 1, 128, 576, 512, 100, 1152, 0.04f, P(A), fo, P(A), aws,
                            nullptr), DSA_ERR_SHAPE);
     (void)dsa_sparse_attn_workspace_size(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX);
+    // masked-dense attention: the workspace holds every token's dense slot list, then the partials
+    const size_t mws = dsa_sparse_attn_masked_dense_workspace_size(2, 1, 128, 512, 4096);
+    EXPECT(mws >= 2u * 4096u * 4u ? DSA_OK : DSA_ERR_SHAPE, DSA_OK);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 512, 4096, 1152, 0.04f, P(A), fo, P(A),
+                                        mws, nullptr), DSA_OK);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 512, 4096, 1152, 0.04f, P(A), fo, P(A),
+                                        mws - 1, nullptr), DSA_ERR_WORKSPACE);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 512, 4096, 1152, 0.04f, P(A), fo,
+                                        nullptr, 0, nullptr), DSA_ERR_WORKSPACE);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 512, DSA_MASKED_DENSE_MAX_SLOTS + 1, 64,
+                                        0.04f, P(A), fo, P(A), mws, nullptr), DSA_ERR_SHAPE);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 528, 4096, 64, 0.04f, P(A), fo, P(A), mws,
+                                        nullptr), DSA_ERR_UNSUPPORTED);
+    EXPECT(dsa_sparse_attn_masked_dense(P(A), P(A), f, io, 2, 1, 128, 576, 512, 4096, 64, 0.04f, P(A), fo, P(A + 8),
+                                        mws, nullptr), DSA_ERR_ALIGN);
+    EXPECT(dsa_sparse_attn_masked_dense_workspace_size(2, 1, 128, 512, DSA_MASKED_DENSE_MAX_SLOTS + 1) == 0
+               ? DSA_OK : DSA_ERR_SHAPE, DSA_OK);
+    (void)dsa_sparse_attn_masked_dense_workspace_size(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX);
+    (void)dsa_sparse_attn_masked_dense_workspace_size(65535, 1, DSA_MAX_ATTN_HEADS, 512, DSA_MASKED_DENSE_MAX_SLOTS);
     int32_t table_storage[4] = {0, 1, 2, 3};
     dsa_paged_cache_t pg{table_storage, 4, 64, 4};
     EXPECT(dsa_sparse_attn_paged(P(A), P(A), f, io, &pg, 2, 1, 16, 192, 128, 256, 64, 0.07f, P(A), fo, P(A), 0,

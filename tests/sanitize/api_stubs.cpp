@@ -24,6 +24,13 @@ hipError_t launch_score_decode_heads(const void*, const float*, const void*, con
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_sparse_attn_masked_dense(const void*, const void*, const float*, const int32_t*, int32_t, int32_t,
+                                           int32_t, int32_t, int32_t, int32_t, int32_t, float, void*, float*, void*,
+                                           hipStream_t)
+{
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_score_prefill_fold(const void*, const float*, const void*, const int32_t*, int32_t, int32_t,
                                      int32_t, int32_t, int32_t, float, float*, hipStream_t)
 {

@@ -94,6 +94,25 @@ def test_topk_validation(lib):
     assert lib.dsa_topk_workspace_size(8192, 8192, 2048) == 0  # many short rows: one workgroup per row
 
 
+def test_masked_dense_attn_validation_and_workspace(lib):
+    f = lib.dsa_sparse_attn_masked_dense
+    need = lib.dsa_sparse_attn_masked_dense_workspace_size(2, 1, 128, 512, 4096)
+    # the dense slot list of each token, then the partials of a 4096-entry list
+    assert need >= 2 * 4096 * 4 + lib.dsa_sparse_attn_workspace_size(2, 1, 128, 512, 4096)
+
+    def call(S_kv=4096, K=64, Dv=512, ws=_p(A), nws=need, q=_p(A)):
+        return f(q, _p(A), None, _p(A), 2, 1, 128, 576, Dv, S_kv, K, 0.1, _p(A), None, ws, nws, None)
+
+    assert call(q=None) == ERR_NULL
+    assert call(Dv=528) == ERR_UNSUPPORTED
+    assert call(K=0) == ERR_SHAPE
+    assert call(S_kv=65537) == ERR_SHAPE
+    assert lib.dsa_sparse_attn_masked_dense_workspace_size(2, 1, 128, 512, 65537) == 0
+    assert call(ws=None, nws=0) == ERR_WORKSPACE
+    assert call(nws=need - 1) == ERR_WORKSPACE
+    assert call(ws=_p(A + 8)) == ERR_ALIGN
+
+
 def test_sparse_attn_validation_and_workspace(lib):
     f = lib.dsa_sparse_attn
 
