@@ -129,6 +129,33 @@ def test_fullsize_prefill(dsa):
     assert np.all(full[:64, :64][tri] == np.float32(oracle.mask_bound()))
 
 
+def test_fullsize_prefill_relu(dsa):
+    """The per-head (ReLU) prefill scorer at 8192 x 8192 on sampled rows: its workgroups take 4
+    consecutive rows, its stages 128 keys in 32-key sub-tiles, and a row's scores leave a stage
+    behind the next stage's key copy; the sample holds the first and last rows, every in-group
+    row position, and rows whose causal limit falls on either side of a stage or sub-tile edge."""
+    w = synthetic.make_workload("prefill")
+    S = w.S_max
+    g = np.random.default_rng(91)
+    rows = set(range(0, 8)) | set(range(S - 8, S))
+    for j, grp in enumerate(g.choice(np.arange(2, S // 4 - 2), size=32, replace=False)):
+        rows.add(4 * int(grp) + j % 4)
+    for m in g.choice(np.arange(1, S // 128), size=12, replace=False):
+        rows.update((128 * int(m) - 1, 128 * int(m), 128 * int(m) + 31, 128 * int(m) + 32))
+    rows = np.array(sorted(rows))
+    announce("prefill full, ReLU per-head scorer: 8192 queries x 8192 keys causal, 64 heads (%d sampled rows)"
+             % len(rows))
+    scores = dsa.dsa_index_score(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), scale=w.index_scale,
+                                 positions=_cuda(w.positions), rows_per_seq=w.rows_per_seq, relu=True)
+    torch.cuda.synchronize()
+    sc = scores[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = oracle.index_score(w.index_q[rows], w.index_w[rows], w.k_cache, scale=w.index_scale,
+                             positions=w.positions[rows], rows_per_seq=len(rows), relu=True)
+    check_scores(sc, ref, rows + 1, oracle.mask_bound())
+    full = scores.cpu().numpy()
+    assert np.isfinite(full).all()
+
+
 def test_fullsize_decode_step(dsa):
     w = synthetic.make_workload("full_decode_step")
     announce("full_decode_step full: 64 x 65536 slots, top-1024 + window 128, 128 heads, 576/512 (sampled)")
