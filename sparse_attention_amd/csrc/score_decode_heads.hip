@@ -22,7 +22,13 @@
 //   * v_mfma_f32_16x16x32_bf16 with M = 16 heads (up to 4 head tiles),
 //     N = 16 slots, K = 32 dims: the row's q is the A operand for the whole
 //     chunk (16 register quads), the keys are the B operand loaded straight
-//     from memory, four tiles in flight.  bf16 keys: lane (slot n, group g)
+//     from memory, four tiles in flight.  Every key load is issued without a
+//     branch around it (lanes past the attendable slots read the tile's last
+//     one, and a wave past its last tile reloads that tile), so the compiler
+//     counts them and each tile waits for its own loads: with the loads under
+//     per-lane and per-tile branches every tile drained all of them (4 x
+//     131072 fp8 slots: 20.6 against 31.8 us; 16 x 32768 bf16: 26.7 against
+//     27.5 us; scores bit-equal).  bf16 keys: lane (slot n, group g)
 //     takes dims 32 t + 8 g .. + 7 in K step t (64 contiguous bytes of the
 //     slot per wave load);
 //   * fp8 keys: lane (n, g) loads bytes 32 g .. 32 g + 31 of the slot and
@@ -110,36 +116,16 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
     const int nht = (H + 15) >> 4;
     constexpr int kSlotBytes = FP8 ? 128 : 256;
 
-    // keys of tile i (slots sb .. sb + 15) as four B operands
+    // The wave's tiles that hold an attendable slot: tiles 0 .. n_my - 1
+    // (tile bases grow with the tile index).
     const int wbase = s0 + 128 * wave;
     auto tile_base = [&](const int i) { return wbase + kChunk * (i >> 3) + 16 * (i & 7); };
-    auto load_tile = [&](const int i, u32x4 (&kb)[4]) {
-        const int sb = tile_base(i);
-        const int s = sb + n;
-        if (s < se) {
-            const uint8_t* p = k + (store_row<PAGED>(pm, r, sb, S_max) + n) * kSlotBytes;
-            if (FP8) {
-                const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + 32 * g);
-                const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + 32 * g + 16);
-                kb[0] = u32x4{x0[0], x0[1], 0u, 0u};  // codes, converted at use
-                kb[1] = u32x4{x0[2], x0[3], 0u, 0u};
-                kb[2] = u32x4{x1[0], x1[1], 0u, 0u};
-                kb[3] = u32x4{x1[2], x1[3], 0u, 0u};
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) kb[t] = *reinterpret_cast<const u32x4*>(p + 64 * t + 16 * g);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) kb[t] = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    u32x4 ring[kAhead][4];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) load_tile(i, ring[i]);
+    int n_my = 0;
+    while (n_my < n_tiles && tile_base(n_my) < se) ++n_my;
 
     // q as A operands: head tile ht, K step t, lane (head n, group g); dims
-    // 32 t + 8 g (bf16 keys) or 32 g + 8 t (fp8 keys, see the header)
+    // 32 t + 8 g (bf16 keys) or 32 g + 8 t (fp8 keys, see the header).  Loaded
+    // first, so the first tile's wait does not reach past them.
     u32x4 qa[kMaxHeadTiles][4];
     float wsc[kMaxHeadTiles][4];  // w[16 ht + 4 g + j] * scale
     const uint16_t* __restrict__ qr = q + (size_t)r * H * 128;
@@ -150,45 +136,80 @@ __global__ __launch_bounds__(kThreads, 2) void score_decode_heads_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int d = FP8 ? 32 * g + 8 * t : 32 * t + 8 * g;
-            qa[ht][t] = h < H ? *reinterpret_cast<const u32x4*>(qr + (size_t)h * 128 + d) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qr + (size_t)(h < H ? h : 0) * 128 + d);
+            qa[ht][t] = h < H ? x : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int hw = 16 * ht + 4 * g + j;
-            wsc[ht][j] = hw < H ? wr[hw] * scale : 0.f;
+            const float wh = wr[hw < H ? hw : 0];  // unconditional: no branch, no early wait
+            wsc[ht][j] = hw < H ? wh * scale : 0.f;
         }
     }
 
+    // Keys of tile i (slots sb .. sb + 15) as four B operands (fp8: its codes,
+    // converted at use, and the slot scales).  Every lane loads: slots past
+    // se read the tile's last attendable slot (same tile, so the same page),
+    // and their scores are never kept.  With no branch around the loads the
+    // compiler counts them and each tile waits for its own loads alone.
+    auto load_tile = [&](const int i, u32x4 (&kb)[4], float& ksc) {
+        const int sb = tile_base(i);
+        const int dn = min(sb + n, se - 1) - sb;
+        const size_t row = store_row<PAGED>(pm, r, sb, S_max) + dn;
+        const uint8_t* p = k + row * kSlotBytes;
+        if (FP8) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + 32 * g);
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + 32 * g + 16);
+            kb[0] = u32x4{x0[0], x0[1], 0u, 0u};
+            kb[1] = u32x4{x0[2], x0[3], 0u, 0u};
+            kb[2] = u32x4{x1[0], x1[1], 0u, 0u};
+            kb[3] = u32x4{x1[2], x1[3], 0u, 0u};
+            ksc = k_scale[row];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kb[t] = *reinterpret_cast<const u32x4*>(p + 64 * t + 16 * g);
+            ksc = 1.f;
+        }
+    };
+    u32x4 ring[kAhead][4];
+    float kring[kAhead];
+    if (n_my > 0) {  // uniform over the wave
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) load_tile(min(u, n_my - 1), ring[u], kring[u]);
 #pragma unroll 1
-    for (int i0 = 0; i0 < n_tiles; i0 += kAhead) {
-        if (tile_base(i0) >= se) break;  // uniform over the wave
+        for (int i0 = 0; i0 < n_my; i0 += kAhead) {
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) {
-            const int i = i0 + u;
-            const int sb = tile_base(i);
-            if (sb >= se) break;  // uniform over the wave
-            u32x4 kb[4];
+            for (int u = 0; u < kAhead; ++u) {
+                const int i = i0 + u;
+                u32x4 kb[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) kb[t] = ring[u][t];
-            if (i + kAhead < n_tiles) load_tile(i + kAhead, ring[u]);
-            if (FP8) {
+                for (int t = 0; t < 4; ++t) kb[t] = ring[u][t];
+                const float ks = kring[u];
+                // the wave's tile kAhead on (its last one again at the end): every
+                // step issues the same loads
+                load_tile(min(i + kAhead, n_my - 1), ring[u], kring[u]);
+                if (i < n_my) {  // uniform over the wave
+                    const int sb = tile_base(i);
+                    if (FP8) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) kb[t] = fp8x8_to_bf16(kb[t][0], kb[t][1]);
-            }
-            const float ks = FP8 ? (sb + n < se ? k_scale[store_row<PAGED>(pm, r, sb, S_max) + n] : 0.f) : 1.f;
-            float acc = 0.f;
+                        for (int t = 0; t < 4; ++t) kb[t] = fp8x8_to_bf16(kb[t][0], kb[t][1]);
+                    }
+                    float acc = 0.f;
 #pragma unroll
-            for (int ht = 0; ht < kMaxHeadTiles; ++ht) {
-                if (ht < nht) {  // uniform
-                    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ht = 0; ht < kMaxHeadTiles; ++ht) {
+                        if (ht < nht) {  // uniform
+                            f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) c = mfma16(qa[ht][t], kb[t], c);
+                            for (int t = 0; t < 4; ++t) c = mfma16(qa[ht][t], kb[t], c);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc = fmaf(wsc[ht][j], fmaxf(FP8 ? c[j] * ks : c[j], 0.f), acc);
+                            for (int j = 0; j < 4; ++j)
+                                acc = fmaf(wsc[ht][j], fmaxf(FP8 ? c[j] * ks : c[j], 0.f), acc);
+                        }
+                    }
+                    acc = lane_group_sum(acc);
+                    if (g == 0 && sb + n < se) stage[sb + n - s0] = acc;
                 }
             }
-            acc = lane_group_sum(acc);
-            if (g == 0 && sb + n < se) stage[sb + n - s0] = acc;
         }
     }
 
