@@ -712,13 +712,19 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     // before the first store.
     constexpr int kMaxPer = DSA_MAX_TOPK / NT;
     int2 ea[kMaxPer], ec[kMaxPer];
+    // Every lane loads (entry 0 of the row's regions where it has nothing to
+    // fetch), so no branch surrounds a load and all of them are in flight
+    // together; with per-lane branches each load drained the previous ones.
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
         const int j = t + u * NT;
-        ea[u] = make_int2(0, -1);
-        if (j < total_gt) ea[u] = rbase[hist[j]];
-        ec[u] = make_int2(0, 0);
-        if (in_lds && j < n_cand) ec[u] = rbase[lcand[j].x];
+        const bool oka = j < total_gt, okc = in_lds && j < n_cand;
+        const int ia = hist[j];                              // j < kMaxPer * NT <= kBins
+        const int ic = lcand[j < kResolveCap ? j : 0].x;
+        const int2 va = rbase[oka ? ia : 0];
+        const int2 vc = rbase[okc ? ic : 0];
+        ea[u] = oka ? va : make_int2(0, -1);
+        ec[u] = okc ? vc : make_int2(0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
