@@ -45,7 +45,32 @@ __device__ __forceinline__ void fold_query(const uint16_t* __restrict__ q, const
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int h = hg; h < H; h += 16) {
+    // the first 64 heads: all loads issued before the first use (heads past H
+    // read head 0 with weight 0), so they cost one memory latency, not four
+    {
+        u32x4 v[4];
+        float wh[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int h = hg + 16 * u;
+            const int hc = h < H ? h : 0;
+            v[u] = *reinterpret_cast<const u32x4*>(q + (size_t)hc * 128 + dblk * 8);
+            wh[u] = w[hc];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float f = hg + 16 * u < H ? wh[u] : 0.f;
+            acc[0] = fmaf(f, bf16_lo(v[u].x), acc[0]);
+            acc[1] = fmaf(f, bf16_hi(v[u].x), acc[1]);
+            acc[2] = fmaf(f, bf16_lo(v[u].y), acc[2]);
+            acc[3] = fmaf(f, bf16_hi(v[u].y), acc[3]);
+            acc[4] = fmaf(f, bf16_lo(v[u].z), acc[4]);
+            acc[5] = fmaf(f, bf16_hi(v[u].z), acc[5]);
+            acc[6] = fmaf(f, bf16_lo(v[u].w), acc[6]);
+            acc[7] = fmaf(f, bf16_hi(v[u].w), acc[7]);
+        }
+    }
+    for (int h = hg + 64; h < H; h += 16) {  // heads 64 .. 127
         const u32x4 v = *reinterpret_cast<const u32x4*>(q + (size_t)h * 128 + dblk * 8);
         const float wh = w[h];
         acc[0] = fmaf(wh, bf16_lo(v.x), acc[0]);
