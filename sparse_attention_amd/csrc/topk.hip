@@ -69,17 +69,33 @@ constexpr int kMaxChunks = 4096;   // chunks per row the resolve's LDS prefix ta
 
 // ---------------------------------------------------------------- helpers
 
+// Inclusive prefix sum over the 64 lanes of a wave on the DPP network: four
+// row shifts within each 16-lane row, then rows 1 and 3 add lane 15 / 47 and
+// rows 2 and 3 add lane 31 (no LDS round trips).
+__device__ __forceinline__ int wave_scan_dpp(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+// Number of lanes below this one whose bit is set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Inclusive prefix sum over a workgroup of NT threads.
 template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
+    v = wave_scan_dpp(v);
     if (lane == 63) wave_tot[wave] = v;
     __syncthreads();
     int add = 0;
@@ -122,60 +138,49 @@ __device__ __forceinline__ float key_to_f32(uint32_t key)
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 // Deterministic output pass of a row path: wave w of NT / 64 owns the slot
 // range [w * span, (w + 1) * span) (span a multiple of 256), a lane takes 4
 // consecutive slots per step.  Each wave counts its slots above the final
 // threshold (gt) and at it (eq); one barrier shares the counts; then each
 // wave emits its range in slot order: gt slots from column (gt count of the
 // lower waves), eq slots from n_gt + (eq count of the lower waves) while
-// fewer than `remaining` are placed.  key4(s) gives the order keys of slots
-// s .. s + 3 (s a multiple of 4; slots >= nv are never used).
+// fewer than `remaining` are placed.  Ranks come from one ballot per slot
+// phase (e = 0..3) and class, counted below each lane with mbcnt, so a
+// step makes no cross-lane LDS round trip.  key4(s) gives the order keys of
+// slots s .. s + 3 (s a multiple of 4; slots >= nv are never used); a
+// position outside [0, k) is never written.
 template <int NT, typename Key4>
 __device__ __forceinline__ void emit_row(Key4 key4, int nv, uint32_t prefix, uint32_t pmask, int k,
                                          int remaining, int wstart, int (*wcnt)[NT / 64], int32_t* __restrict__ orow,
                                          float* __restrict__ osc)
 {
-    const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int span = ((nv + NT / 64 - 1) / (NT / 64) + 255) & ~255;
     const int lo = wave * span;
     const int hi = min(lo + span, nv);
-    int c_gt = 0, c_eq = 0;
-    for (int s0 = lo; s0 < hi; s0 += 256) {  // wave-uniform trip count
-        const int s = s0 + 4 * lane;
-        if (s < hi) {
-            const u32x4 kk = key4(s);
+    // per-slot-phase ballots: bit l of gt[e] / eq[e] is slot s0 + 4 l + e
+    auto classify = [&](int s, u32x4 kk, uint64_t* gt, uint64_t* eq) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t km = kk[e] & pmask;
-                const bool in = s + e < hi;
-                c_gt += (in && km > prefix) ? 1 : 0;
-                c_eq += (in && km == prefix) ? 1 : 0;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t km = kk[e] & pmask;
+            const bool in = s + e < hi;
+            gt[e] = __ballot(in && km > prefix);
+            eq[e] = __ballot(in && km == prefix);
+        }
+    };
+    int c_gt = 0, c_eq = 0;  // wave-uniform
+    for (int s0 = lo; s0 < hi; s0 += 256) {
+        const int s = s0 + 4 * (threadIdx.x & 63);
+        const u32x4 kk = key4(s < hi ? s : lo);
+        uint64_t gt[4], eq[4];
+        classify(s, kk, gt, eq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            c_gt += __popcll(gt[e]);
+            c_eq += __popcll(eq[e]);
         }
     }
-    c_gt = wave_sum(c_gt);
-    c_eq = wave_sum(c_eq);
-    if (lane == 0) {
+    if ((threadIdx.x & 63) == 0) {
         wcnt[0][wave] = c_gt;
         wcnt[1][wave] = c_eq;
     }
@@ -187,40 +192,39 @@ __device__ __forceinline__ void emit_row(Key4 key4, int nv, uint32_t prefix, uin
     }
     const int n_gt = k - remaining;
     for (int s0 = lo; s0 < hi; s0 += 256) {
-        const int s = s0 + 4 * lane;
-        u32x4 kk = {0u, 0u, 0u, 0u};
-        int fl = 0;  // bit e: slot s + e is gt; bit 4 + e: eq
-        if (s < hi) {
-            kk = key4(s);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t km = kk[e] & pmask;
-                const bool in = s + e < hi;
-                fl |= (in && km > prefix) ? (1 << e) : 0;
-                fl |= (in && km == prefix) ? (16 << e) : 0;
-            }
-        }
-        const int mine = __popc(fl & 15) | (__popc(fl >> 4) << 16);  // this lane's gt | eq << 16
-        const int incl = wave_inclusive_scan(mine);
-        const int tot = __shfl(incl, 63, 64);
-        int g = bgt + ((incl - mine) & 0xFFFF);
-        int q = beq + ((incl - mine) >> 16);
+        const int s = s0 + 4 * (threadIdx.x & 63);
+        const u32x4 kk = key4(s < hi ? s : lo);
+        uint64_t gt[4], eq[4];
+        classify(s, kk, gt, eq);
+        int g = bgt, q = beq;  // this lane's first gt / eq rank
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            g += lanes_below(gt[e]);
+            q += lanes_below(eq[e]);
+        }
+        const uint32_t lb = 1u << (threadIdx.x & 31);
+        const int hl = (threadIdx.x >> 5) & 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool is_gt = (uint32_t)(gt[e] >> (32 * hl)) & lb;
+            const bool is_eq = (uint32_t)(eq[e] >> (32 * hl)) & lb;
             int pos = -1;
-            if (fl & (1 << e)) {
+            if (is_gt) {
                 pos = g++;
-            } else if (fl & (16 << e)) {
+            } else if (is_eq) {
                 if (q < remaining) pos = n_gt + q;
                 ++q;
             }
-            if (pos >= 0) {
+            if (pos >= 0 && pos < k) {
                 orow[pos] = emit(s + e, wstart);
                 if (osc) osc[pos] = key_to_f32(kk[e]);
             }
         }
-        bgt += tot & 0xFFFF;
-        beq += tot >> 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bgt += __popcll(gt[e]);
+            beq += __popcll(eq[e]);
+        }
     }
 }
 
@@ -328,9 +332,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 }
 
 // Row path for rows of at most kRowCap slots (16-byte aligned): the row is
-// read once with 16-byte loads into LDS as order keys, building the first
-// digit's histogram on the way; later digits and the output pass run on LDS.
-// Outputs are placed in slot order by emit_row (one barrier per row).
+// read once with 16-byte loads, all of a thread's loads in flight before the
+// first wait, into LDS as order keys, building the first digit's histogram
+// on the way; later digits (16-byte LDS reads) and the output pass run on
+// LDS.  Outputs are placed in slot order by emit_row (one barrier per row).
 __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     const float* __restrict__ scores, int32_t S_max, const int32_t* __restrict__ positions, int32_t valid_len,
     int32_t k, int32_t window, int32_t* __restrict__ out_idx, float* __restrict__ out_scores)
@@ -367,16 +372,29 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
     for (int i = t; i < kBins; i += NT) hist[i] = 0;
     __syncthreads();
     const int nv4 = (nv + 3) & ~3;  // <= S_max (a multiple of 4)
-    for (int s = 4 * t; s < nv4; s += 4 * NT) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + s);
-        u32x4 kk;
+    {
+        // every load of the row in flight at once (addresses clamped into the row), then the keys
+        constexpr int kPer = kRowCap / (4 * NT);
+        u32x4 v[kPer];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t key = f32_order_key(__uint_as_float(v[e]));
-            kk[e] = key;
-            if (s + e < nv) atomicAdd(&hist[key >> 20], 1);
+        for (int i = 0; i < kPer; ++i) {
+            const int s = 4 * t + i * 4 * NT;
+            v[i] = *reinterpret_cast<const u32x4*>(row + (s < nv4 ? s : 0));
         }
-        *reinterpret_cast<u32x4*>(keys + s) = kk;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int s = 4 * t + i * 4 * NT;
+            if (s < nv4) {
+                u32x4 kk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = f32_order_key(__uint_as_float(v[i][e]));
+                    kk[e] = key;
+                    if (s + e < nv) atomicAdd(&hist[key >> 20], 1);
+                }
+                *reinterpret_cast<u32x4*>(keys + s) = kk;
+            }
+        }
     }
     __syncthreads();
 
@@ -390,9 +408,11 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
         if (pass > 0) {
             for (int i = t; i < nb; i += NT) hist[i] = 0;
             __syncthreads();
-            for (int s = t; s < nv; s += NT) {
-                const uint32_t key = keys[s];
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & (nb - 1)], 1);
+            for (int s = 4 * t; s < nv4; s += 4 * NT) {
+                const u32x4 kk = *reinterpret_cast<const u32x4*>(keys + s);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (s + e < nv && (kk[e] & pmask) == prefix) atomicAdd(&hist[(kk[e] >> sh) & (nb - 1)], 1);
             }
             __syncthreads();
         }
@@ -645,13 +665,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_resolve_kernel(
     for (int c0 = 0; c0 < nch; c0 += NT) {
         const int c = c0 + t;
         const int2 n = c >= nch ? make_int2(0, 0) : (c0 == 0 ? n_first : crow[c]);
-        const long long v = (long long)n.x | ((long long)n.y << 32);
-        long long x = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const long long y = __shfl_up(x, off, 64);
-            if ((t & 63) >= off) x += y;
-        }
+        // each count of a row is below 2^24: two 32-bit wave scans, packed after
+        const long long x = (long long)(uint32_t)wave_scan_dpp(n.x) | ((long long)wave_scan_dpp(n.y) << 32);
         if ((t & 63) == 63) wave_tot64[t >> 6] = x;
         __syncthreads();
         long long add = carry, tot = carry;
