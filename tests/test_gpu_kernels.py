@@ -166,7 +166,7 @@ def test_score_prefill_several_sequences_with_offset(dsa):
 # e.g. 8 x 65536 runs 2048-slot chunks and 8 x 300000 4096-slot ones); one
 # workgroup per row re-reading the row otherwise
 @pytest.mark.parametrize("S_max,k", [(100, 1), (5000, 64), (33000, 1024), (65536, 2048), (40002, 512),
-                                     (70000, 2048), (3000, 2048), (300000, 2048)])
+                                     (70000, 2048), (3000, 2048), (300000, 2048), (8192, 2048), (8188, 333)])
 def test_topk_edges(dsa, S_max, k):
     g = np.random.default_rng(S_max * 7 + k)
     nvs = sorted({0, 1, max(0, k - 1), k, k + 1, S_max // 2, S_max - 1, S_max})
