@@ -509,6 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
 // are placed on the XCDs as in the main kernel (XCD x takes the x-th run of
 // ceil(BS / kXcds) tokens), so a token's partial results are read back from
 // the L2 that wrote them.
+template <int NS>
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml, const float* __restrict__ sink,
     int32_t BS, int32_t Hq, int32_t Dv, int32_t nsplit, uint16_t* __restrict__ out, float* __restrict__ lse)
@@ -519,34 +520,34 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     if (lw >= tok_per_xcd * Hq || tok >= BS) return;  // uniform over the wave
     const int lane = threadIdx.x & 63;
     const int head = lw % Hq;
-    // every load in flight at once: the (max, sum) pairs and this lane's
-    // first 8 output dims of every split (a split without entries holds
-    // zeros and gets weight 0)
-    float2 ml[kMaxSplits];
-    u32x4 v0[kMaxSplits];
-    const bool first = 8 * lane < Dv;
+    // Every load in flight at once: the sink, the (max, sum) pairs and this
+    // lane's first 8 output dims of every split (a split without entries
+    // holds zeros and gets weight 0).  The loads are unconditional, from
+    // clamped addresses (split 0 stands in for splits past nsplit, dim 0 for
+    // lanes past Dv), so no branch makes the compiler wait between them.
+    const int nsp = NS == kMaxSplits ? nsplit : NS;  // the two-split instance knows its count
+    float2 ml[NS];
+    u32x4 v0[NS];
+    const int d0 = 8 * lane < Dv ? 8 * lane : 0;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < nsplit) {
-            const size_t ph = ((size_t)tok * nsplit + s) * Hq + head;
-            ml[s] = part_ml[ph];
-            v0[s] = first ? *reinterpret_cast<const u32x4*>(part_o + ph * Dv + 8 * lane) : u32x4{0, 0, 0, 0};
-        }
+    for (int s = 0; s < NS; ++s) {
+        const size_t ph = ((size_t)tok * nsp + (s < nsp ? s : 0)) * Hq + head;
+        ml[s] = part_ml[ph];
+        v0[s] = *reinterpret_cast<const u32x4*>(part_o + ph * Dv + d0);
     }
-    const float sk = sink ? sink[head] * kLog2e : -INFINITY;
+    const float sk = sink ? sink[head] * kLog2e : -INFINITY;  // (after the others: its branch waits)
+    // weights by selects, so that both halves of every pair are needed at once
     float M = sk;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        if (s < nsplit) M = fmaxf(M, ml[s].x);
-    float wgt[kMaxSplits];
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, s < nsp ? ml[s].x : -INFINITY);
+    float wgt[NS];
     float den = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        wgt[s] = 0.f;
-        if (s < nsplit) {
-            if (ml[s].y > 0.f) wgt[s] = ml[s].y * exp2f(ml[s].x - M);
-            den += wgt[s];
-        }
+    for (int s = 0; s < NS; ++s) {
+        const bool use = s < nsp && ml[s].y > 0.f;
+        const float e = exp2f(use ? ml[s].x - M : 0.f);
+        wgt[s] = use ? ml[s].y * e : 0.f;
+        den += wgt[s];
     }
     if (M != -INFINITY) den += exp2f(sk - M);
     const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -554,10 +555,10 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(
     for (int d = 8 * lane; d < Dv; d += 512) {
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            if (s < nsplit) {
+        for (int s = 0; s < NS; ++s) {
+            if (s < nsp) {
                 const u32x4 v = d == 8 * lane ? v0[s] : *reinterpret_cast<const u32x4*>(
-                    part_o + (((size_t)tok * nsplit + s) * Hq + head) * Dv + d);
+                    part_o + (((size_t)tok * nsp + s) * Hq + head) * Dv + d);
                 const float f = wgt[s] * inv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -602,8 +603,13 @@ hipError_t launch_variant(const void* q, const void* kv, const float* attn_sink,
         K_top, sm_scale, ns, static_cast<uint16_t*>(out), lse, part_o, part_ml, pm);
     if (ns > 1) {
         const long long waves_per_xcd = tok_per_xcd * Hq;
-        sparse_attn_combine_kernel<<<(unsigned)((waves_per_xcd + 3) / 4 * kXcds), 256, 0, stream>>>(
-            part_o, part_ml, attn_sink, BS, Hq, Dv, ns, static_cast<uint16_t*>(out), lse);
+        const unsigned cgrid = (unsigned)((waves_per_xcd + 3) / 4 * kXcds);
+        if (ns == 2)
+            sparse_attn_combine_kernel<2><<<cgrid, 256, 0, stream>>>(part_o, part_ml, attn_sink, BS, Hq, Dv, ns,
+                                                                    static_cast<uint16_t*>(out), lse);
+        else
+            sparse_attn_combine_kernel<kMaxSplits><<<cgrid, 256, 0, stream>>>(part_o, part_ml, attn_sink, BS, Hq, Dv,
+                                                                             ns, static_cast<uint16_t*>(out), lse);
     }
     return hipGetLastError();
 }
