@@ -168,3 +168,53 @@ def test_decode_step_graph_replays(dsa, static_scratch):
             _same(a, b, "graph replay %d %s" % (rep, what))
         _disturb()
         torch.cuda.synchronize()
+
+
+def test_workspace_contents_do_not_matter(dsa):
+    """Whatever the caller's workspace holds on entry (here all 0xFF bytes, then zeros), the results are the
+    same: every call clears the state it accumulates into (the top-k histograms and counters) itself, and the
+    attention's split partials are written before they are read."""
+    g = np.random.default_rng(11)
+    sc = torch.from_numpy(g.standard_normal((8, 50000)).astype(np.float32)).cuda()
+    nws = dsa.topk_workspace_bytes(8, 50000, 1000)
+    assert nws > 0  # the chunked path
+    announce("workspace contents: dsa_topk 8 x 50000 k=1000")
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+    a = dsa.dsa_topk(sc, 1000, workspace=ws).clone()
+    ws.zero_()
+    b = dsa.dsa_topk(sc, 1000, workspace=ws)
+    torch.cuda.synchronize()
+    _same(a, b, "top-k row")
+
+    S_kv, K_top = 2048, 1152
+    for B in (64, 8):  # two splits, eight splits
+        q = torch.from_numpy(g.standard_normal((B, 1, 128, 576)).astype(np.float32)).to(torch.bfloat16).cuda()
+        kv = torch.from_numpy((0.5 * g.standard_normal((B, S_kv, 576))).astype(np.float32)).to(torch.bfloat16).cuda()
+        sink = torch.from_numpy(g.standard_normal(128).astype(np.float32)).cuda()
+        idx = torch.from_numpy(g.integers(-1, S_kv, (B, 1, K_top)).astype(np.int32)).cuda()
+        nws = dsa.sparse_attn_workspace_bytes(B, 1, 128, 512, K_top)
+        assert nws > 0  # split lists
+        announce("workspace contents: dsa_sparse_attn B=%d K_top=%d" % (B, K_top))
+        ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+        o1, l1 = dsa.dsa_sparse_attn(q, kv, sink, idx, sm_scale=576 ** -0.5, dv=512, with_lse=True, workspace=ws)
+        o1, l1 = o1.clone(), l1.clone()
+        ws.zero_()
+        o2, l2 = dsa.dsa_sparse_attn(q, kv, sink, idx, sm_scale=576 ** -0.5, dv=512, with_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        _same(o1, o2, "attention output")
+        _same(l1, l2, "attention lse")
+
+    w = synthetic.make_workload("full_decode_step", B=16, S_max=32768, topk=1024, window=128)
+    announce("workspace contents: dsa_decode_step B=16 S_max=32768")
+    step = dsa.DecodeStep(_cuda(w.index_q), _cuda(w.index_w), _cuda(w.k_cache), positions=_cuda(w.positions),
+                          valid_len=w.valid_len, index_scale=w.index_scale, index_topk=w.index_topk,
+                          window=w.window, q=_cuda(w.q), kv=_cuda(w.kv), attn_sink=_cuda(w.sink),
+                          sm_scale=w.sm_scale, dv=w.dv)
+    step._ws.fill_(0xFF)
+    step()
+    first = [t.clone() for t in (step.index_list, step.out, step.lse)]
+    step._ws.zero_()
+    step()
+    torch.cuda.synchronize()
+    for a, b, what in zip(first, (step.index_list, step.out, step.lse), ("index list", "output", "lse")):
+        _same(a, b, "decode step " + what)
