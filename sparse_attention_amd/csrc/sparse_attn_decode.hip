@@ -44,7 +44,10 @@
 //     = entry): DMA row addresses come from a lane shuffle, the mask from a
 //     ballot.
 //   * split partial outputs are stored as bf16 and rounded once more in the
-//     combine.  Measured on two tokens of the full decode step (with the
+//     combine.  For the MLA shape they leave through LDS (the freed KV
+//     buffers): each wave transposes its 16 heads x 512 values into rows and
+//     writes 16 contiguous 1 KiB rows with 16-byte stores, instead of 32
+//     8-byte stores that each touch 16 rows.  Measured on two tokens of the full decode step (with the
 //     64-entry kernel, both ways): fp32 partials gave a worst output error
 //     of 3.2e-4 and a relative L2 error of 2.4e-3, bf16 partials 3.6e-4 and
 //     2.9e-3, against a tolerance of 2e-2 absolute; bf16 halves the partial
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     if (nblk == 0) wait_vmem();  // the index prefetch
 
     const float l_tot = group_sum(l_run);
-    if (!head_ok) return;
     if (nsplit == 1) {
+        if (!head_ok) return;
         const float sk = sink ? sink[head] * kLog2e : -INFINITY;
         float inv = 0.f, den = 0.f;
         if (m_run != -INFINITY) {
@@ -491,17 +494,47 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn_kernel(
     // partial result of this split: normalised output, (max, sum) in log2 units
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const size_t ph = ((size_t)tok * nsplit + split) * Hq + head;
-    uint16_t* prow = part_o + ph * Dv;
+    if (EXACT && VT == 32 && Hq % 64 == 0) {
+        // Transposed through LDS (the KV buffers are free once every wave is
+        // past its last block): each wave writes its 16 heads x 512 values
+        // as 16 contiguous 1 KiB rows with 16-byte stores.  Rows are padded
+        // to 1040 bytes, so the 8-byte writes of the 16 heads hit distinct banks.
+        constexpr int kRowB = 1040;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's operand reads are done
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        char* tb = reinterpret_cast<char*>(wave_u < 2 ? kvbuf0 : kvbuf1) + (wave_u & 1) * 16 * kRowB;
 #pragma unroll
-    for (int v = 0; v < VT; ++v) {
-        if (v < vtiles) {
+        for (int v = 0; v < VT; ++v) {
             uint2 w;
             w.x = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
             w.y = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
-            *reinterpret_cast<uint2*>(prow + 16 * v + 4 * g) = w;
+            *reinterpret_cast<uint2*>(tb + n * kRowB + 2 * (16 * v + 4 * g)) = w;
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        uint16_t* pbase = part_o + (((size_t)tok * nsplit + split) * Hq + hg * kHeadsPerGroup + wave_u * 16) * Dv;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(tb + h * kRowB + 16 * lane);
+            *reinterpret_cast<u32x4*>(pbase + (size_t)h * Dv + 8 * lane) = x;
+        }
+    } else {
+        if (!head_ok) return;
+        uint16_t* prow = part_o + ph * Dv;
+#pragma unroll
+        for (int v = 0; v < VT; ++v) {
+            if (v < vtiles) {
+                uint2 w;
+                w.x = pack_bf16x2(acc[v][0] * inv, acc[v][1] * inv);
+                w.y = pack_bf16x2(acc[v][2] * inv, acc[v][3] * inv);
+                *reinterpret_cast<uint2*>(prow + 16 * v + 4 * g) = w;
+            }
         }
     }
-    if (g == 0) part_ml[ph] = make_float2(m_run, l_tot);
+    if (head_ok && g == 0) part_ml[ph] = make_float2(m_run, l_tot);
 }
 
 // Merge the nsplit partial results of every (token, head): one wave per
