@@ -44,14 +44,14 @@
 //     = entry): DMA row addresses come from a lane shuffle, the mask from a
 //     ballot.
 //   * split partial outputs are stored as bf16 and rounded once more in the
-//     combine.  For the MLA shape they leave through LDS (the freed KV
-//     buffers): each wave transposes its 16 heads x 512 values into rows and
-//     writes 16 contiguous 1 KiB rows with 16-byte stores, instead of 32
-//     8-byte stores that each touch 16 rows.  Measured on two tokens of the full decode step (with the
+//     combine.  Measured on two tokens of the full decode step (with the
 //     64-entry kernel, both ways): fp32 partials gave a worst output error
 //     of 3.2e-4 and a relative L2 error of 2.4e-3, bf16 partials 3.6e-4 and
 //     2.9e-3, against a tolerance of 2e-2 absolute; bf16 halves the partial
-//     bytes.
+//     bytes.  For the MLA shape the partials leave through LDS (the freed KV
+//     buffers): each wave transposes its 16 heads x 512 values into rows and
+//     writes 16 contiguous 1 KiB rows with 16-byte stores, instead of 32
+//     8-byte stores that each touch 16 rows.
 //   * paged KV (a block table maps each page of a sequence's slots to a page
 //     of a shared pool): a pool may exceed 4 GiB, which one buffer
 //     descriptor cannot span (buffer offsets, also of structured buffers,
