@@ -151,7 +151,9 @@ dsa_status_t dsa_index_score(const void* q, const float* w, const void* k_cache,
  * for column, on every call (ties at the boundary included).
  *
  * Limits: 1 <= index_topk <= DSA_MAX_TOPK; M >= 1;
- * 1 <= S_max <= DSA_MAX_TOPK_SLOTS.
+ * 1 <= S_max <= DSA_MAX_TOPK_SLOTS.  The workspace (size from
+ * dsa_topk_workspace_size; 0 for many short rows) must be 16-byte aligned
+ * (DSA_ERR_ALIGN otherwise); its contents on entry do not matter.
  */
 size_t dsa_topk_workspace_size(int32_t M, int32_t S_max, int32_t index_topk);
 dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32_t* positions,

@@ -247,6 +247,7 @@ dsa_status_t dsa_topk(const float* scores, int32_t M, int32_t S_max, const int32
     if (s != DSA_OK) return s;
     const size_t need = dsa::plan::topk_workspace_bytes(M, S_max);
     if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return DSA_ERR_ALIGN;
     return launch_status(dsa::launch_topk(scores, M, S_max, positions, valid_len, index_topk, 0, topk_idx,
                                           topk_scores, workspace, false, stream));
 }

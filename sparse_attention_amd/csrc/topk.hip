@@ -432,11 +432,14 @@ __global__ __launch_bounds__(kRowLdsThreads) void topk_row_lds_kernel(
 
 // ---------------------------------------------------------------- chunked path
 
-__global__ __launch_bounds__(256) void topk_clear_kernel(uint32_t* __restrict__ ws, int32_t n_words)
+// Zero n_quads 16-byte units (the header is a whole number of them per row
+// and the workspace is 16-byte aligned).
+__global__ __launch_bounds__(256) void topk_clear_kernel(u32x4* __restrict__ ws, int32_t n_quads)
 {
     const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n_words) ws[i] = 0u;
+    if (i < n_quads) ws[i] = u32x4{0u, 0u, 0u, 0u};
 }
+static_assert(kHeaderWords % 4 == 0, "the header clear writes 16-byte units");
 
 template <int CHUNK>
 __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(
@@ -828,8 +831,9 @@ hipError_t launch_topk(const float* scores, int32_t M, int32_t S_max, const int3
     const int n_counts = (int)plan::topk_count_words(S_max);
     int2* counts = reinterpret_cast<int2*>(ghist + (size_t)M * kHeaderWords);
     int2* cand = counts + (size_t)M * n_counts;
-    const int n_words = M * kHeaderWords;
-    if (!header_zeroed) topk_clear_kernel<<<(n_words + 255) / 256, 256, 0, stream>>>(ghist, n_words);
+    const int n_quads = M * (kHeaderWords / 4);
+    if (!header_zeroed)
+        topk_clear_kernel<<<(n_quads + 255) / 256, 256, 0, stream>>>(reinterpret_cast<u32x4*>(ghist), n_quads);
     // chunk size: 4096 slots, or 2048 when that would leave the chip short of workgroups
     if (plan::topk_chunk(M, S_max) == kChunkSmall) {
         const dim3 grid((S_max + kChunkSmall - 1) / kChunkSmall, M);

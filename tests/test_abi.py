@@ -91,6 +91,7 @@ def test_topk_validation(lib):
     assert need >= 16 * 32768 * 4
     assert f(_p(A), 16, 32768, None, -1, 1024, _p(A), None, None, 0, None) == ERR_WORKSPACE
     assert f(_p(A), 16, 32768, None, -1, 1024, _p(A), None, _p(A), need - 1, None) == ERR_WORKSPACE
+    assert f(_p(A), 16, 32768, None, -1, 1024, _p(A), None, _p(A + 8), need, None) == ERR_ALIGN
     assert lib.dsa_topk_workspace_size(8192, 8192, 2048) == 0  # many short rows: one workgroup per row
 
 
